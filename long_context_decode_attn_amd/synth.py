@@ -1,0 +1,285 @@
+"""Seeded synthetic inputs for R-SWA / SR-SWA decode attention.
+
+This module holds the input recipe only: workload shapes, random streams,
+bf16 rounding of the drawn values and the planted-block construction used to
+make routing non-trivial.  It contains none of the attention, routing or
+entmax arithmetic; both the GPU path and the CPU checker read the same bits
+produced here.
+
+Workload shapes follow the pages' deployments: 256 visual tokens per page
+(Unlimited OCR paper summary, lshu.cn, section 3.1 DeepEncoder), documents of
+2 to 125 pages inside the 32K context, a generated-token window of n = 128
+(same page, section 2.1 core design), up to 512 concurrent sequences (same
+page, section 5.2 TPS), 32-token blocks and 16 routed blocks (Unlimited-OCR-2
+explainer, nxmr.cn, section on sparse routing).  No document, image or trained
+weight is used: every value is drawn from N(0, 1) (the index projection from
+N(0, 1/32)) with numpy's PCG64 under a fixed seed.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+TOKENS_PER_PAGE = 256
+BLOCK = 32
+WINDOW = 128
+
+# Independent random streams; the value is the first element of the
+# SeedSequence spawn key, the second is the sequence index (or the step).
+_S_PROJ, _S_QSTAR, _S_KP, _S_VP, _S_RING, _S_STEP, _S_PLANT, _S_Q, _S_MISC = range(9)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    dtype: str            # "f32" or "bf16": storage type of q, k, v and out
+    pages: int
+    prompt: int           # prompt tokens appended to the visual tokens
+    t0: int               # generated tokens before the first decode step
+    steps: int
+    seed: int
+    sparse: bool = False
+    window: int = WINDOW
+    idx_dim: int = 32
+    block: int = BLOCK
+    topk: int = 16
+    planted: int = 0      # planted relevant blocks per sequence
+    planted_on_pages: bool = False   # one planted block per distinct page
+    fixed_query: bool = False        # same query every step (the planted q*)
+
+    @property
+    def prefix_len(self) -> int:
+        return self.pages * TOKENS_PER_PAGE + self.prompt
+
+    @property
+    def n_blocks(self) -> int:
+        return -(-self.prefix_len // self.block)
+
+    @property
+    def units(self) -> int:
+        return self.batch * self.heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads.  Names say what they are; sizes are in the fields.
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in [
+        # dense, CPU-sized, fp32: 2 pages + 16 prompt tokens, ring starts
+        # empty and wraps three times in 512 steps
+        Workload("dense-2p-b1-fp32", batch=1, heads=2, head_dim=64, dtype="f32",
+                 pages=2, prompt=16, t0=0, steps=512, seed=1001),
+        # dense steady state: 10 pages + 32 prompt, ring full at t = 6144
+        Workload("dense-10p-b64", batch=64, heads=10, head_dim=128, dtype="bf16",
+                 pages=10, prompt=32, t0=6144, steps=1000, seed=1002),
+        # dense, high concurrency, short context: 1 page + 32 prompt
+        Workload("dense-1p-b512", batch=512, heads=10, head_dim=128, dtype="bf16",
+                 pages=1, prompt=32, t0=128, steps=1000, seed=1003),
+        # SR-SWA at 40 pages: 320 blocks, 16 planted per sequence
+        Workload("srswa-40p-b32", batch=32, heads=10, head_dim=128, dtype="bf16",
+                 pages=40, prompt=0, t0=128, steps=1000, seed=1004, sparse=True,
+                 planted=16, fixed_query=True),
+        # SR-SWA at 125 pages (32000 tokens, 1000 blocks), 24 planted blocks on
+        # 24 distinct pages; 2048 steps wrap the ring 16 times
+        Workload("srswa-125p-b8", batch=8, heads=10, head_dim=128, dtype="bf16",
+                 pages=125, prompt=0, t0=128, steps=2048, seed=1005, sparse=True,
+                 planted=24, planted_on_pages=True, fixed_query=True),
+    ]
+}
+
+
+# ----------------------------------------------------------------------------
+# bf16 storage
+# ----------------------------------------------------------------------------
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even);
+    returns the 16-bit patterns as uint16."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def store(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage form of float32 values: float32 for "f32", uint16 bf16 bits for "bf16"."""
+    return np.ascontiguousarray(x32, dtype=np.float32) if dtype == "f32" else to_bf16_bits(x32)
+
+
+def widen(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored elements."""
+    if dtype == "f32":
+        return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    return bf16_bits_to_f32(stored).astype(np.float64)
+
+
+NAN_BITS = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0)}
+
+
+def nan_fill(shape, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.full(shape, np.nan, dtype=np.float32)
+    return np.full(shape, 0x7FC0, dtype=np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# random streams
+# ----------------------------------------------------------------------------
+def _gen(seed: int, *key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(entropy=seed, spawn_key=tuple(key))))
+
+
+def normal32(seed: int, shape, *key: int) -> np.ndarray:
+    return _gen(seed, *key).standard_normal(size=shape, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# static state: prefix K/V, projection, planted blocks, fixed queries
+# ----------------------------------------------------------------------------
+def projection(w: Workload) -> np.ndarray:
+    """Index projection P [head_dim][idx_dim], float32, entries N(0, 1/idx_dim)."""
+    p = normal32(w.seed, (w.head_dim, w.idx_dim), _S_PROJ, 0)
+    return (p * np.float32(1.0 / math.sqrt(w.idx_dim))).astype(np.float32)
+
+
+def planted_blocks(w: Workload, b: int) -> np.ndarray:
+    """Sorted block indices whose keys carry the planted query shift."""
+    if w.planted == 0:
+        return np.zeros(0, dtype=np.int64)
+    g = _gen(w.seed, _S_PLANT, b)
+    if w.planted_on_pages:
+        per_page = TOKENS_PER_PAGE // w.block
+        pages = [(i * w.pages) // w.planted for i in range(w.planted)]
+        blocks = [p * per_page + int(g.integers(0, per_page)) for p in pages]
+        return np.array(sorted(blocks), dtype=np.int64)
+    return np.sort(g.choice(w.n_blocks, size=w.planted, replace=False)).astype(np.int64)
+
+
+def fixed_query_f32(w: Workload, b: int) -> np.ndarray:
+    """The planted query q*[h][D] of sequence b, already rounded to storage precision."""
+    q = normal32(w.seed, (w.heads, w.head_dim), _S_QSTAR, b)
+    return widen(store(q, w.dtype), w.dtype).astype(np.float32)
+
+
+def prefix_kv_seq(w: Workload, b: int, m_cap: Optional[int] = None):
+    """Prefix K and V of sequence b as storage arrays [H][m_cap][D]; planted
+    blocks get k <- round(k + 0.5 q*_h)."""
+    m = w.prefix_len
+    m_cap = m if m_cap is None else m_cap
+    k = normal32(w.seed, (w.heads, m, w.head_dim), _S_KP, b)
+    v = normal32(w.seed, (w.heads, m, w.head_dim), _S_VP, b)
+    if w.planted:
+        qs = fixed_query_f32(w, b)
+        for blk in planted_blocks(w, b):
+            lo, hi = blk * w.block, min(blk * w.block + w.block, m)
+            k[:, lo:hi, :] += np.float32(0.5) * qs[:, None, :]
+    ks, vs = store(k, w.dtype), store(v, w.dtype)
+    if m_cap > m:
+        pad = nan_fill((w.heads, m_cap - m, w.head_dim), w.dtype)
+        ks = np.concatenate([ks, pad], axis=1)
+        vs = np.concatenate([vs, pad], axis=1)
+    return ks, vs
+
+
+def prefix_kv(w: Workload, m_cap: Optional[int] = None):
+    """Prefix K, V storage arrays [B][H][m_cap][D] (padding beyond m is NaN)."""
+    m_cap = w.prefix_len if m_cap is None else m_cap
+    shape = (w.batch, w.heads, m_cap, w.head_dim)
+    dt = np.float32 if w.dtype == "f32" else np.uint16
+    K = np.empty(shape, dtype=dt)
+    V = np.empty(shape, dtype=dt)
+    for b in range(w.batch):
+        K[b], V[b] = prefix_kv_seq(w, b, m_cap)
+    return K, V
+
+
+# ----------------------------------------------------------------------------
+# generated tokens: history before t0 and per-step inputs
+# ----------------------------------------------------------------------------
+def history_token(w: Workload, tau: int):
+    """k, v of generated token tau for every (b, h): storage arrays [B][H][D].
+    Tokens tau < t0 form the initial ring, tokens >= t0 are appended by steps."""
+    k = normal32(w.seed, (w.batch, w.heads, w.head_dim), _S_RING, tau, 0)
+    v = normal32(w.seed, (w.batch, w.heads, w.head_dim), _S_RING, tau, 1)
+    return store(k, w.dtype), store(v, w.dtype)
+
+
+def step_query(w: Workload, step: int) -> np.ndarray:
+    """Query of decode step `step` (0-based), storage array [B][H][D]."""
+    if w.fixed_query:
+        q = np.stack([fixed_query_f32(w, b) for b in range(w.batch)]).astype(np.float32)
+        return store(q, w.dtype)
+    return store(normal32(w.seed, (w.batch, w.heads, w.head_dim), _S_Q, step), w.dtype)
+
+
+def step_inputs(w: Workload, step: int):
+    """(q, k_new, v_new) of decode step `step`; k_new, v_new are token t0+step."""
+    k, v = history_token(w, w.t0 + step)
+    return step_query(w, step), k, v
+
+
+def initial_ring(w: Workload):
+    """Ring K/V [B][H][n][D] holding tokens max(0, t0-n) .. t0-1 in slot tau mod n
+    (slots never written are NaN) and the generated count t_gen[B] = t0."""
+    n = w.window
+    Kr = nan_fill((w.batch, w.heads, n, w.head_dim), w.dtype)
+    Vr = nan_fill((w.batch, w.heads, n, w.head_dim), w.dtype)
+    for tau in range(max(0, w.t0 - n), w.t0):
+        k, v = history_token(w, tau)
+        Kr[:, :, tau % n, :] = k
+        Vr[:, :, tau % n, :] = v
+    t_gen = np.full((w.batch,), w.t0, dtype=np.int32)
+    return Kr, Vr, t_gen
+
+
+def step_pool(w: Workload, steps: int):
+    """Stacked per-step inputs for `steps` consecutive steps: q, k_new, v_new
+    as storage arrays [steps][B][H][D]."""
+    qs, ks, vs = [], [], []
+    for s in range(steps):
+        q, k, v = step_inputs(w, s)
+        qs.append(q)
+        ks.append(k)
+        vs.append(v)
+    return np.stack(qs), np.stack(ks), np.stack(vs)
+
+
+def random_scores(seed: int, units: int, nb_cap: int, spread: float = 1.0) -> np.ndarray:
+    """Block scores [units][nb_cap] float32 for exercising the selection step
+    on its own: N(0, spread^2)."""
+    return (normal32(seed, (units, nb_cap), _S_MISC, 0) * np.float32(spread)).astype(np.float32)
+
+
+def random_selection(seed: int, units: int, n_blocks: int, k: int, live: int):
+    """A routing result for exercising sparse decode on its own: per unit, k
+    distinct ascending block indices (-1 padding when n_blocks < k) and a
+    log-weight bias per entry; `live` entries chosen at random get a bias drawn
+    from U(-5, 0), the rest -inf.  Returns (idx int32 [units][k],
+    bias float32 [units][k])."""
+    g = _gen(seed, _S_MISC, 1)
+    idx = np.full((units, k), -1, dtype=np.int32)
+    bias = np.full((units, k), -np.inf, dtype=np.float32)
+    for u in range(units):
+        sel = np.sort(g.choice(n_blocks, size=min(k, n_blocks), replace=False))
+        idx[u, :len(sel)] = sel
+        order = g.permutation(len(sel))[:live]
+        bias[u, order] = g.uniform(-5.0, 0.0, size=len(order)).astype(np.float32)
+    return idx, bias

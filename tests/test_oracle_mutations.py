@@ -1,0 +1,133 @@
+"""Planted mistakes: each test hands a pin a broken copy of one oracle
+routine (a dropped term, an off-by-one, a wrong sign or index, a transposed
+operand) and checks that the pin rejects it.  Mistakes are planted only in
+these CPU copies, never in the GPU path."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import uocr_oracle as O
+from tests import test_oracle_pins as T
+
+
+def _fails(check, **broken):
+    with pytest.raises(AssertionError):
+        check(**broken)
+
+
+def test_window_off_by_one_is_caught():
+    _fails(T.check_ring, window_positions=lambda t, n: list(range(max(0, t - n + 1), t)))
+
+
+def test_ring_read_from_wrong_slot_is_caught():
+    def ring_window(ring, t):
+        n = ring.shape[0]
+        return np.stack([ring[(tau + 1) % n] for tau in O.window_positions(t, n)]) if t else ring[:0]
+    _fails(T.check_ring, ring_window=ring_window)
+
+
+def test_append_before_pointer_advance_is_caught():
+    def ring_append(rk, rv, t_gen, k, v):
+        n = rk.shape[2]
+        for b in range(rk.shape[0]):
+            t_gen[b] += 1
+            rk[b, :, t_gen[b] % n] = k[b]
+            rv[b, :, t_gen[b] % n] = v[b]
+    _fails(T.check_ring, ring_append=ring_append)
+
+
+def test_cache_law_without_min_is_caught():
+    _fails(T.check_cache_law, cache_len=lambda m, n, t: m + n)
+
+
+def test_attention_without_scale_is_caught():
+    _fails(T.check_attention, attention=lambda q, K, V, s, bias=None: O.attention(q, K, V, 1.0, bias))
+
+
+def test_attention_with_sign_error_is_caught():
+    _fails(T.check_attention, attention=lambda q, K, V, s, bias=None: O.attention(-q, K, V, s, bias))
+
+
+def test_attention_dropping_bias_is_caught():
+    _fails(T.check_attention, attention=lambda q, K, V, s, bias=None: O.attention(q, K, V, s, None))
+
+
+def test_rswa_missing_prefix_is_caught():
+    def rswa_decode(q, Kp, Vp, pl, rk, rv, t, s):
+        return O.rswa_decode(q, Kp, Vp, np.zeros_like(pl), rk, rv, t, s)
+    _fails(T.check_rswa_reductions, rswa_decode=rswa_decode)
+
+
+def test_block_mean_over_fixed_32_is_caught():
+    def block_index(K, m, P, block=32):
+        Pd = np.asarray(P, float)
+        return np.array([(np.asarray(K, float)[lo:lo + block] @ Pd).sum(0) / block
+                         for lo in range(0, m, block)])
+    _fails(T.check_block_index, block_index=block_index)
+
+
+def test_score_with_extra_temperature_is_caught():
+    def block_scores(q, P, kbar):
+        return O.block_scores(q, P, kbar) / math.sqrt(np.asarray(kbar).shape[1])
+    _fails(T.check_block_index, block_scores=block_scores)
+
+
+def test_block_index_mean_before_wrong_axis_is_caught():
+    def block_index(K, m, P, block=32):
+        Pd = np.asarray(P, float)
+        return np.array([(np.asarray(K, float)[lo:min(lo + block, m)] @ Pd).mean(1).mean() * np.ones(Pd.shape[1])
+                         for lo in range(0, m, block)])
+    _fails(T.check_block_index, block_index=block_index)
+
+
+def test_entmax_without_half_is_caught():
+    def entmax(z):
+        return O.entmax15(2 * np.asarray(z, float))
+    _fails(T.check_entmax, entmax=entmax)
+
+
+def test_entmax_as_softmax_is_caught():
+    def entmax(z):
+        e = np.exp(np.asarray(z, float) - np.max(z))
+        return e / e.sum()
+    _fails(T.check_entmax, entmax=entmax)
+
+
+def test_entmax_as_sparsemax_is_caught():
+    def sparsemax(z):
+        z = np.asarray(z, float)
+        zs = np.sort(z)[::-1]
+        cs = np.cumsum(zs)
+        r = np.arange(1, len(z) + 1)
+        k = r[1 + r * zs > cs].max()
+        tau = (cs[k - 1] - 1) / k
+        return np.maximum(z - tau, 0)
+    _fails(T.check_entmax, entmax=sparsemax)
+
+
+def test_topk_with_wrong_tie_break_is_caught():
+    def topk(s, k):
+        order = sorted(range(len(s)), key=lambda j: (-float(s[j]), -j))
+        return sorted(order[:min(k, len(s))])
+    _fails(T.check_topk, topk_blocks=topk)
+
+
+def test_topk_ascending_scores_is_caught():
+    def topk(s, k):
+        order = sorted(range(len(s)), key=lambda j: (float(s[j]), j))
+        return sorted(order[:min(k, len(s))])
+    _fails(T.check_topk, topk_blocks=topk)
+
+
+def test_srswa_bias_before_scale_is_caught():
+    def srswa_unit(q, K, V, m, sel, bias, wk, wv, scale, block=32):
+        b2 = None if bias is None else np.asarray(bias, float) / scale
+        return O.srswa_unit(q, K, V, m, sel, b2, wk, wv, scale, block)
+    _fails(T.check_srswa, srswa_unit=srswa_unit)
+
+
+def test_srswa_missing_window_is_caught():
+    def srswa_unit(q, K, V, m, sel, bias, wk, wv, scale, block=32):
+        return O.srswa_unit(q, K, V, m, sel, bias, wk[:0], wv[:0], scale, block)
+    _fails(T.check_srswa, srswa_unit=srswa_unit)
