@@ -1,0 +1,306 @@
+"""Decode-attention benchmark of the R-SWA / SR-SWA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode fused|separate]
+
+A step is one pass of the decode hot path over one batch: ring append, then
+(SR-SWA) block scores, 1.5-entmax top-k and sparse decode, or (R-SWA) dense
+decode.  The block index is built once per layer before timing (it depends
+only on the static prefix).  Steps rotate over --layers independent per-layer
+decode states, as a decoder does while generating one token, so that a
+step's working set has left the 256 MB Infinity Cache before the same layer
+is visited again: bandwidth figures are HBM figures, not cache hits.
+
+The K timed steps are replayed from HIP graphs (as a serving loop runs decode
+steps); eager host-launched
+throughput is reported beside it.  Prints one JSON line: throughput in
+attention unit-steps per second (units = batch x heads), the roofline of the
+dominant kernel (algorithmic bytes over its average duration, from HIP events
+around the timed region) and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
+METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
+UNIT = "steps/s (batch×heads)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2400)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="srswa-40p-b32")
+    ap.add_argument("--layers", type=int, default=12, help="independent per-layer states cycled by the steps")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--mode", choices=["fused", "separate"], default="fused",
+                    help="fused: one uocr_*_step launch per step; separate: one launch per row")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes per launch (what each kernel must move)
+# ----------------------------------------------------------------------------
+def algorithmic_bytes(w, live_blocks_per_unit=None):
+    """Bytes each kernel must read + write per launch for the workload."""
+    units, D, es, n = w.units, w.head_dim, w.elem_bytes, w.window
+    row = D * es
+    wnd = min(n, w.t0 + 1)   # window size during the steps (ring full in every benchmark workload)
+    b = {"uocr_ring_append": units * (2 * row + 2 * row) + w.batch * 8}
+    if w.sparse:
+        nb, k = w.n_blocks, w.topk
+        b["uocr_block_score"] = units * (row + nb * w.idx_dim * 4 + nb * 4) + D * w.idx_dim * 4 + w.batch * 4
+        b["uocr_entmax15_topk"] = units * (nb * 4 + k * 12) + w.batch * 4
+        live = units * min(k, nb) if live_blocks_per_unit is None else int(live_blocks_per_unit)
+        b["uocr_srswa_decode"] = (units * (row + k * 8 + 2 * wnd * row + row) + live * 2 * w.block * row
+                                  + w.batch * 8)
+    else:
+        b["uocr_rswa_decode"] = units * (row + 2 * (w.prefix_len + wnd) * row + row) + w.batch * 8
+    return b
+
+
+def index_bytes(w):
+    return w.units * (w.prefix_len * w.head_dim * w.elem_bytes + w.n_blocks * w.idx_dim * 4)
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample
+# ----------------------------------------------------------------------------
+def cpu_baseline(w, budget_s: float):
+    """Time the oracle's decode step (append, score from the prebuilt block
+    index, entmax top-k, sparse or dense attention) on a sample of units, one
+    unit-step at a time, until the time budget is spent."""
+    from threadpoolctl import threadpool_limits
+
+    from long_context_decode_attn_amd import synth as S
+    from oracle import uocr_oracle as O
+
+    rng = np.random.default_rng(0)
+    n_sample = 4
+    seqs = sorted(set(int(x) for x in rng.choice(w.batch, size=min(n_sample, w.batch), replace=False)))
+    P = S.projection(w).astype(np.float64) if w.sparse else None
+    units = []
+    for b in seqs:
+        Kp, Vp = S.prefix_kv_seq(w, b)
+        Kp, Vp = S.widen(Kp, w.dtype), S.widen(Vp, w.dtype)
+        h = int(rng.integers(w.heads))
+        Kr, Vr, t_gen = S.initial_ring(w)
+        u = {"b": b, "h": h, "Kp": Kp[h], "Vp": Vp[h],
+             "Kr": S.widen(Kr[b:b + 1, h:h + 1], w.dtype), "Vr": S.widen(Vr[b:b + 1, h:h + 1], w.dtype),
+             "t": t_gen[b:b + 1].astype(np.int64).copy()}
+        if w.sparse:
+            u["kbar"] = O.block_index(u["Kp"], w.prefix_len, P)   # one-time, not timed
+        units.append(u)
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        step = 0
+        while time.perf_counter() - t0 < budget_s:
+            q, k, v = S.step_inputs(w, step)
+            for u in units:
+                b, h = u["b"], u["h"]
+                O.ring_append(u["Kr"], u["Vr"], u["t"], S.widen(k[b:b + 1, h:h + 1], w.dtype),
+                              S.widen(v[b:b + 1, h:h + 1], w.dtype))
+                qd = S.widen(q[b, h], w.dtype)
+                t = int(u["t"][0])
+                wk, wv = O.ring_window(u["Kr"][0, 0], t), O.ring_window(u["Vr"][0, 0], t)
+                if w.sparse:
+                    s32 = O.as_f32(O.block_scores(qd, P, u["kbar"]))
+                    idx, _, bias = O.route_unit(s32, w.topk)
+                    O.srswa_unit(qd, u["Kp"], u["Vp"], w.prefix_len, idx, bias, wk, wv, w.scale)
+                else:
+                    O.rswa_unit(qd, u["Kp"], u["Vp"], w.prefix_len, wk, wv, w.scale)
+                done += 1
+            step += 1
+        dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": f"{done} unit-steps ({len(units)} (sequence, head) units x {step} steps) of {w.name} "
+                      f"in {dt:.1f} s, float64 numpy, 1 thread; block index built before timing"}
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode path has no "
+              f"cross-GPU step; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_decode_attn_amd import synth as S
+    from long_context_decode_attn_amd import uocr as U
+    from long_context_decode_attn_amd.session import DecodeSession, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    U.load_library()
+    torch.cuda.set_device(0)
+    w = S.WORKLOADS[args.workload]
+    t_setup = time.perf_counter()
+    fused = args.mode == "fused"
+    base = DecodeSession(w, num_splits=args.num_splits, fused=fused)
+    layers = [base] + [base.clone() for _ in range(args.layers - 1)]
+    torch.cuda.synchronize()
+
+    # one-time block index per layer (timed on its own, reported separately)
+    idx_ms = None
+    if w.sparse:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in layers:
+            s.build_index()
+        e1.record()
+        torch.cuda.synchronize()
+        idx_ms = e0.elapsed_time(e1) / len(layers)
+
+    pool_n = 64
+    qp, kp, vp = S.step_pool(w, pool_n)
+    pool = [(to_device(qp[i], w.dtype), to_device(kp[i], w.dtype), to_device(vp[i], w.dtype)) for i in range(pool_n)]
+    setup_s = time.perf_counter() - t_setup
+
+    def run_step(i):
+        s = layers[i % len(layers)]
+        q, k, v = pool[i % pool_n]
+        s.step(q, k, v)
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    # ---- eager (host-launched) throughput, for reference ----
+    n_eager = min(args.steps, 500)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_eager):
+        run_step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms_per_step = e0.elapsed_time(e1) / n_eager
+
+    # ---- HIP graph of G steps (two per layer, so the double-buffered
+    # generated-token counts of the fused steps return to their buffers) ----
+    G = 2 * len(layers)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(G):
+            run_step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps, rest = divmod(args.steps, G)
+    tail = None
+    if rest:   # the last K mod G steps, one step on each of the first layers
+        tail = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(tail):
+            for i in range(rest):
+                run_step(i)
+        tail.replay()
+        torch.cuda.synchronize()
+    steps = reps * G + rest
+
+    # ---- timed region: exactly K steps ----
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    if tail is not None:
+        tail.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop)
+    ms_per_step = ms / steps
+    value = w.units * steps / (ms / 1e3)
+
+    # ---- per-kernel durations ----
+    if fused:
+        # one kernel per step: its average duration in the timed region
+        names = ["uocr_srswa_step" if w.sparse else "uocr_rswa_step"]
+        kern_ms = {names[0]: ms_per_step}
+    else:
+        # separate launches: HIP events around each launch (eager; adds the
+        # event overhead to every kernel)
+        names = ["uocr_ring_append"] + (["uocr_block_score", "uocr_entmax15_topk", "uocr_srswa_decode"]
+                                        if w.sparse else ["uocr_rswa_decode"])
+        nk = min(args.steps, 500)
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+              for _ in range(nk)]
+        torch.cuda.synchronize()
+        for i in range(nk):
+            s = layers[i % len(layers)]
+            q, k, v = pool[i % pool_n]
+            calls = [lambda: s.append(k, v)]
+            if w.sparse:
+                calls += [lambda: s.score(q), s.select, lambda: s.attend(q)]
+            else:
+                calls += [lambda: s.attend(q)]
+            for (a, b), c in zip(ev[i], calls):
+                a.record()
+                c()
+                b.record()
+        torch.cuda.synchronize()
+        kern_ms = {n: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(nk)]))
+                   for j, n in enumerate(names)}
+
+    live = None
+    if w.sparse:
+        sb = base.sel_bias.cpu().numpy()
+        si = base.sel_idx.cpu().numpy()
+        live = int(np.sum((si >= 0) & np.isfinite(sb)))
+    abytes = algorithmic_bytes(w, live)
+    if fused:   # the step kernel moves what the rows it fuses move (scores stay on chip)
+        rows = dict(abytes)
+        total = sum(rows.values())
+        if w.sparse:
+            total -= 2 * w.units * w.n_blocks * 4
+        abytes = {names[0]: total}
+    kernels = {n: {"avg_us": round(kern_ms[n] * 1e3, 3), "algorithmic_bytes": abytes[n],
+                   "gbs": round(abytes[n] / (kern_ms[n] * 1e-3) / 1e9, 1)} for n in names}
+    dom = max(names, key=lambda n: kern_ms[n])
+    achieved = abytes[dom] / (kern_ms[dom] * 1e-3) / 1e9
+    step_bytes = sum(abytes.values())
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "prefix_tokens": w.prefix_len, "pages": w.pages, "window": w.window,
+                   "sparse": w.sparse, "topk": w.topk if w.sparse else None,
+                   "block": w.block if w.sparse else None, "layers_cycled": len(layers),
+                   "splits": (U.uocr_srswa_splits(base.shape, base.route, args.num_splits) if w.sparse
+                              else U.uocr_rswa_splits(base.shape, args.num_splits)),
+                   "mode": args.mode, "accumulate": "f32 attention, f64 routing",
+                   "parallelism": "single-gpu"},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "step_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "timing": (f"HIP graph of {G} steps replayed {reps} times" + (f" + {rest} steps" if rest else "")
+                   + f"; eager launches: {eager_ms_per_step * 1e3:.2f} us/step"),
+        "eager_ms_per_step": round(eager_ms_per_step, 5),
+        "kernels": kernels,
+    }
+    if w.sparse:
+        result["routing"] = {"live_blocks_per_unit": round(live / w.units, 3),
+                             "index_build_ms_per_layer": round(idx_ms, 4),
+                             "index_build_gbs": round(index_bytes(w) / (idx_ms * 1e-3) / 1e9, 1)}
+    result["setup_s"] = round(setup_s, 1)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * uocr.h -- C ABI of libuocr.so: single-step decode attention for Reference
+ * Sliding Window Attention (R-SWA) and its sparse variant (SR-SWA) on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (sources are web pages, cited by title and section):
+ *   - R-SWA: each decode query attends to a permanent reference prefix of m
+ *     tokens (visual tokens + prompt; always visible, never evicted, never
+ *     updated) and to a causal window of the last n generated tokens, default
+ *     n = 128, so the cache holds m + min(n, T) tokens after T generated
+ *     tokens.  ["百度Unlimited OCR" paper summary, lshu.cn/news/33052,
+ *     section 二 (R-SWA), parts 1 and 2; "百度 Unlimited OCR 深度实战",
+ *     chenxutan.com/d/4055.html, sections 2.2.1 and 3.3.1.]
+ *   - The window is a ring buffer: the new token overwrites the oldest slot
+ *     in place and the write pointer advances circularly.  [Unlimited-OCR-2
+ *     explainer, nxmr.cn/news/162408, section "环形缓冲"; the chenxutan.com
+ *     page, section 3.3.2, keeps it as a deque of maximum length n.]
+ *   - SR-SWA: the prefix is cut into 32-token blocks; a light low-dimensional
+ *     index projection scores every block against the query; 1.5-entmax over
+ *     the scores picks the top-k (16) blocks, 16 x 32 = 512 reference tokens;
+ *     each block's weight enters the attention logits of its tokens as a log
+ *     bias.  [nxmr.cn/news/162408, section "稀疏路由", steps 1-4.]
+ *
+ * Conventions for every call
+ *   - All tensors are device pointers to contiguous arrays, innermost
+ *     dimension last; q, k, v and out share the element type of
+ *     uocr_shape.dtype (fp32 or bf16, bf16 = upper 16 bits of an IEEE fp32,
+ *     rounded to nearest even).  Arithmetic is fp32 with fp32 softmax
+ *     accumulation; routing (index, scores, entmax) accumulates in fp64.
+ *   - Unit = one (sequence b, head h) pair; units are ordered b-major.
+ *   - Layouts: q, out, k_new, v_new [B][H][D]; k_prefix, v_prefix
+ *     [B][H][prefix_cap][D]; k_ring, v_ring [B][H][window][D];
+ *     prefix_len, t_gen [B] int32; proj [D][idx_dim] fp32; kbar_idx
+ *     [B][H][nb_cap][idx_dim] fp32 with nb_cap = ceil(prefix_cap/block_size);
+ *     scores [B][H][nb_cap] fp32; sel_idx [B][H][topk] int32; sel_prob,
+ *     sel_bias [B][H][topk] fp32.
+ *   - Pointers to q/k/v/out/ring/prefix/kbar/proj must be 16-byte aligned.
+ *   - Device-side values are clamped, never trusted for addressing:
+ *     prefix_len[b] to [0, prefix_cap], t_gen[b] below 0 to 0, sel_idx
+ *     entries outside [0, ceil(prefix_len[b]/block_size)) are skipped.
+ *   - Ownership: the caller allocates and owns every buffer; the library
+ *     allocates nothing, keeps no state except a thread-local error string,
+ *     never synchronises the stream, and returns as soon as the work is
+ *     enqueued on `stream` (a hipStream_t passed as void*; NULL = default
+ *     stream).
+ *   - Errors: every call validates its arguments on the host before any
+ *     launch and returns a negative uocr_status without launching anything
+ *     on failure; uocr_last_error() then describes it.  A launch failure
+ *     reported by the runtime returns UOCR_ERR_HIP.  Faults inside kernels
+ *     surface at the caller's next synchronisation.
+ */
+#ifndef UOCR_H
+#define UOCR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UOCR_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+  UOCR_OK = 0,
+  UOCR_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  UOCR_ERR_SHAPE = -2,       /* a size is out of the supported range           */
+  UOCR_ERR_DTYPE = -3,       /* unknown element type                           */
+  UOCR_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required     */
+  UOCR_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned        */
+  UOCR_ERR_UNSUPPORTED = -6, /* a valid but unimplemented configuration        */
+  UOCR_ERR_HIP = -7          /* the HIP runtime rejected a launch              */
+} uocr_status;
+
+typedef enum { UOCR_F32 = 0, UOCR_BF16 = 1 } uocr_dtype;
+
+/* Problem shape shared by every call.
+ *   batch B >= 1, heads H >= 1 (one KV head per query head), head_dim D in
+ *   {64, 128}; prefix_cap = token capacity of the prefix arrays per unit
+ *   (0 .. 2^20); window n in 1 .. 1024; dtype a uocr_dtype; scale = logit
+ *   scale (normally 1/sqrt(D)), finite.  B*H must not exceed 2^24.        */
+typedef struct {
+  int32_t batch;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t prefix_cap;
+  int32_t window;
+  int32_t dtype;
+  float scale;
+} uocr_shape;
+
+/* Routing configuration of SR-SWA.  block_size must be 32 (the pages'
+ * sparse_block_size), idx_dim must be 32, topk in 1 .. 64; topk >= the number
+ * of blocks selects every block.  nb_cap = ceil(prefix_cap / 32) <= 4096.   */
+typedef struct {
+  int32_t block_size;
+  int32_t idx_dim;
+  int32_t topk;
+} uocr_route;
+
+/* ---------------------------------------------------------------------------
+ * uocr_ring_append -- append one generated token per sequence to the ring.
+ * [nxmr.cn/news/162408 "环形缓冲": overwrite the oldest slot in place, the
+ * write pointer advances circularly; chenxutan.com 3.3.2: deque(maxlen=n).]
+ *   For every b: slot = t_gen[b] mod window; k_ring[b][h][slot][:] =
+ *   k_new[b][h][:] and the same for v, for all h; then t_gen[b] += 1.
+ *   Token tau therefore always lives in slot tau mod window.  Mutates
+ *   k_ring, v_ring, t_gen (in place); t_gen[b] must stay below 2^31 - 1.
+ *   Call it before the decode of the same step (append-then-attend).       */
+int uocr_ring_append(const uocr_shape* shape, void* k_ring, void* v_ring,
+                     const void* k_new, const void* v_new, int32_t* t_gen,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Workspace of the dense decode: when a unit's keys are cut into several
+ * workgroups (splits), each leaves its (max, sum, partial output) in the
+ * caller's workspace and a second kernel in the same stream merges them.
+ * Size from uocr_rswa_workspace_bytes (0 when one split suffices: then the
+ * workspace may be NULL).  No initialisation is needed.  Calls that overlap
+ * in time on one workspace race: give concurrent streams their own.        */
+/* Workgroups per unit of the dense decode: num_splits > 0 is taken as given
+ * (bounded to one workgroup per 64 keys), 0 picks one from the shape.        */
+int32_t uocr_rswa_splits(const uocr_shape* shape, int32_t num_splits);
+size_t uocr_rswa_workspace_bytes(const uocr_shape* shape, int32_t num_splits);
+
+/* ---------------------------------------------------------------------------
+ * uocr_rswa_decode -- dense R-SWA decode attention for one step.
+ * [lshu.cn/news/33052 section 二.1-2; chenxutan.com 2.2.1 and 3.3.1.]
+ *   For unit (b, h) with m = prefix_len[b] and w = min(window, t_gen[b]):
+ *   keys = k_prefix[b][h][0..m) followed by ring slots 0..w-1 (the visible
+ *   window; order does not affect the result), logits l_j = scale * q.k_j,
+ *   out = sum_j softmax(l)_j v_j.  An empty key set (m = 0 and t_gen = 0)
+ *   gives out = 0.  The key set is cut into splits processed in parallel and
+ *   merged by log-sum-exp.                                                  */
+int uocr_rswa_decode(const uocr_shape* shape, const void* q,
+                     const void* k_prefix, const void* v_prefix,
+                     const int32_t* prefix_len, const void* k_ring,
+                     const void* v_ring, const int32_t* t_gen, void* out,
+                     void* workspace, size_t ws_bytes, int32_t num_splits,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * uocr_block_index_build -- block keys of the prefix, once after prefill.
+ * [nxmr.cn/news/162408 "稀疏路由" steps 1-2: 32-token blocks, low-dimensional
+ * index projection.]
+ *   kbar_idx[b][h][j][:] = proj^T * mean_{t in block j} k_prefix[b][h][t][:]
+ *   for j < ceil(m/32) (a last partial block averages its valid tokens);
+ *   rows j >= ceil(m/32) up to nb_cap are set to 0.  fp64 accumulation,
+ *   stored as fp32.  The prefix is static, so this runs once per sequence. */
+int uocr_block_index_build(const uocr_shape* shape, const uocr_route* route,
+                           const void* k_prefix, const int32_t* prefix_len,
+                           const float* proj, float* kbar_idx, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * uocr_block_score -- relevance of every prefix block to the query.
+ * [nxmr.cn/news/162408 "稀疏路由" step 2.]
+ *   q_idx = proj^T q; scores[b][h][j] = q_idx . kbar_idx[b][h][j] for
+ *   j < ceil(m/32), -inf for the rest of nb_cap.  No scale.  fp64
+ *   accumulation, rounded once to fp32.                                     */
+int uocr_block_score(const uocr_shape* shape, const uocr_route* route,
+                     const void* q, const float* proj, const float* kbar_idx,
+                     const int32_t* prefix_len, float* scores, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * uocr_entmax15_topk -- 1.5-entmax over the block scores and top-k selection.
+ * [nxmr.cn/news/162408 "稀疏路由" steps 3-4; 1.5-entmax as in Peters,
+ * Niculae & Martins 2019, exact threshold by sorting.]
+ *   p = entmax_1.5(scores[b][h][0..nb)) with nb = ceil(m/32), i.e.
+ *   p_j = max(0, s_j/2 - tau)^2 with sum_j p_j = 1.  The min(topk, nb) blocks
+ *   ranked first by (score descending, index ascending) are written to
+ *   sel_idx in ascending index order with sel_prob = p_j and sel_bias = ln p_j
+ *   (-inf where p_j = 0); no renormalisation over the kept blocks.  Entries
+ *   past min(topk, nb) are idx -1, prob 0, bias -inf.  sel_prob may be NULL.
+ *   The threshold is computed in fp64 from the fp32 scores.                 */
+int uocr_entmax15_topk(const uocr_shape* shape, const uocr_route* route,
+                       const float* scores, const int32_t* prefix_len,
+                       int32_t* sel_idx, float* sel_prob, float* sel_bias,
+                       void* stream);
+
+/* ---------------------------------------------------------------------------
+ * uocr_srswa_decode -- SR-SWA decode: selected blocks + window, log bias.
+ * [nxmr.cn/news/162408 "稀疏路由" step 4 and "环形缓冲"; 16 x 32 = 512
+ * reference tokens per query.]
+ *   keys = the tokens of every selected block j (sel_idx entry i >= 0), with
+ *   bias sel_bias[i] added to the scaled logit of each of its tokens, plus
+ *   the visible window with bias 0; out = softmax-weighted sum of values.
+ *   sel_bias NULL means bias 0 for every selected block.  A block whose bias
+ *   is -inf has weight exactly 0 and is not read at all.  One workgroup per
+ *   unit; num_splits = waves per workgroup (0 = default 8, at most 8).    */
+int32_t uocr_srswa_splits(const uocr_shape* shape, const uocr_route* route, int32_t num_splits);
+int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route,
+                      const void* q, const void* k_prefix, const void* v_prefix,
+                      const int32_t* prefix_len, const int32_t* sel_idx,
+                      const float* sel_bias, const void* k_ring,
+                      const void* v_ring, const int32_t* t_gen, void* out,
+                      int32_t num_splits, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused decode steps: one call = one whole decode step of the path above.
+ * [Same passages as the calls they fuse.]
+ *   uocr_rswa_step  == uocr_ring_append then uocr_rswa_decode;
+ *   uocr_srswa_step == uocr_ring_append then uocr_block_score,
+ *                      uocr_entmax15_topk and uocr_srswa_decode,
+ * with the same results (sel_idx / sel_prob / sel_bias / out), except that
+ * the generated-token counts are double-buffered: t_gen_in[b] is read,
+ * t_gen_out[b] = t_gen_in[b] + 1 is written and t_gen_in is left unchanged,
+ * so that no workgroup can see a count another one already advanced.  The
+ * two arrays must not overlap; callers alternate them between steps.  The
+ * sparse step keeps the block scores on chip (no scores array).
+ *   uocr_rswa_step: workspace and num_splits as for uocr_rswa_decode.
+ *   uocr_srswa_step: one workgroup per unit; num_splits = waves per
+ *   workgroup, 4 or 8 (0 = 8).                                              */
+int uocr_rswa_step(const uocr_shape* shape, const void* q, const void* k_new,
+                   const void* v_new, const void* k_prefix, const void* v_prefix,
+                   const int32_t* prefix_len, void* k_ring, void* v_ring,
+                   const int32_t* t_gen_in, int32_t* t_gen_out, void* out,
+                   void* workspace, size_t ws_bytes, int32_t num_splits,
+                   void* stream);
+int uocr_srswa_step(const uocr_shape* shape, const uocr_route* route,
+                    const void* q, const void* k_new, const void* v_new,
+                    const void* k_prefix, const void* v_prefix,
+                    const int32_t* prefix_len, const float* proj,
+                    const float* kbar_idx, void* k_ring, void* v_ring,
+                    const int32_t* t_gen_in, int32_t* t_gen_out,
+                    int32_t* sel_idx, float* sel_prob, float* sel_bias,
+                    void* out, int32_t num_splits, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics. */
+const char* uocr_status_string(int status); /* static string, never NULL   */
+const char* uocr_last_error(void);          /* thread-local detail, "" if none */
+int uocr_version(void);                     /* UOCR_VERSION                */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UOCR_H */

@@ -1,0 +1,101 @@
+// Internal interface between the C-ABI layer (uocr_api.cpp) and the gfx950
+// kernels (uocr_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace uocr {
+
+struct AppendArgs {
+  void* k_ring;
+  void* v_ring;
+  const void* k_new;
+  const void* v_new;
+  int32_t* t_gen;
+  int batch, heads, window;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_prefix;
+  const void* v_prefix;
+  const int32_t* prefix_len;
+  const void* k_ring;
+  const void* v_ring;
+  const int32_t* t_gen;
+  void* out;
+  float* part_ml;      // dense with splits > 1: [units][splits][2] (max, sum)
+  float* part_o;       // dense with splits > 1: [units][splits][D]
+  int units, heads, prefix_cap, window;
+  int splits;          // dense: workgroups per unit (1 for sparse)
+  int chunk;           // dense: keys per split
+  int waves;           // waves per workgroup
+  float qscale;        // scale * log2(e)
+  // sparse only
+  const int32_t* sel_idx;
+  const float* sel_bias;
+  int topk;
+};
+
+struct IndexArgs {
+  const void* k_prefix;
+  const int32_t* prefix_len;
+  const float* proj;
+  float* kbar;
+  int units, heads, prefix_cap, nb_cap;
+};
+
+struct ScoreArgs {
+  const void* q;
+  const float* proj;
+  const float* kbar;
+  const int32_t* prefix_len;
+  float* scores;
+  int units, heads, prefix_cap, nb_cap;
+  int parts;           // workgroups per unit
+};
+
+struct TopkArgs {
+  const float* scores;
+  const int32_t* prefix_len;
+  int32_t* sel_idx;
+  float* sel_prob;
+  float* sel_bias;
+  int units, heads, prefix_cap, nb_cap, topk;
+};
+
+// A fused decode step: DecodeArgs plus the new token, the double-buffered
+// generated-token counts and (SR-SWA) the routing inputs and outputs.
+struct StepArgs {
+  DecodeArgs d;        // d.k_ring / d.v_ring alias k_ring / v_ring below
+  const void* k_new;
+  const void* v_new;
+  void* k_ring;
+  void* v_ring;
+  const int32_t* t_gen_in;
+  int32_t* t_gen_out;
+  const float* proj;
+  const float* kbar;
+  int nb_cap;
+  int32_t* sel_idx;
+  float* sel_prob;
+  float* sel_bias;
+};
+
+constexpr int kBlock = 32;     // tokens per routing block
+constexpr int kIdxDim = 32;    // index projection width
+constexpr int kMaxBlocks = 4096;
+constexpr int kMaxTopk = 64;
+
+hipError_t launch_ring_append(int dtype, int head_dim, const AppendArgs& a, hipStream_t s);
+hipError_t launch_rswa_decode(int dtype, int head_dim, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_srswa_decode(int dtype, int head_dim, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_block_index(int dtype, int head_dim, const IndexArgs& a, hipStream_t s);
+hipError_t launch_block_score(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s);
+hipError_t launch_entmax_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_srswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
+hipError_t launch_rswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
+
+}  // namespace uocr

@@ -1,0 +1,1489 @@
+// gfx950 (CDNA4) kernels for R-SWA / SR-SWA single-step decode attention.
+//
+// Decode attention here is a memory-bound matrix-vector product (one query
+// per (sequence, head)), so the kernels are built around streaming K/V rows
+// from HBM with 16-byte loads per lane, not around MFMA:
+//   * one head row (D = 128 bf16 = 256 B) is read by 16 lanes, a wave64 covers
+//     4 rows per load instruction and keeps U such loads of K and of V in
+//     flight before using any of them;
+//   * the q.k dot product is reduced across the 16 lanes of a row with
+//     cross-lane shuffles, the softmax is online (running max / sum in the
+//     base-2 domain) per group of rows and merged across groups at the end;
+//   * the waves of a workgroup take disjoint slices of a unit's keys and
+//     merge their (max, sum, partial output) through LDS by log-sum-exp; the
+//     dense decode can also cut a unit into several workgroups, whose partials
+//     a second, small kernel merges.  No device-wide fence or atomic is used:
+//     on gfx950 every agent-scope fence writes back and invalidates the L2.
+//
+// Method sources (web pages): R-SWA key set = permanent prefix + last n
+// generated tokens ("百度Unlimited OCR" paper summary, lshu.cn, section 二);
+// ring buffer overwriting the oldest slot (Unlimited-OCR-2 explainer,
+// nxmr.cn, section "环形缓冲"); 32-token blocks, index-projection scores,
+// 1.5-entmax top-k and log bias (same explainer, section "稀疏路由").
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "uocr_internal.h"
+
+namespace uocr {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Floor of the running maximum: finite, so that exp2(m_old - m_new) never
+// sees (-inf) - (-inf).  Logits (scaled, biased, base 2) are far above it.
+constexpr float kFloor = -1.0e30f;
+constexpr int kWaves = 4;  // waves per workgroup of the block-index kernel
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// element types and row geometry
+// ---------------------------------------------------------------------------
+// DT 0 = fp32, 1 = bf16.  A lane handles one 16-byte chunk of a row.
+template <int DT, int D>
+struct Geo {
+  static constexpr int ES = DT == 0 ? 4 : 2;  // bytes per element
+  static constexpr int E = 16 / ES;           // elements per lane chunk
+  static constexpr int LPR = D * ES / 16;     // lanes per row
+  static constexpr int RPL = 64 / LPR;        // rows per wave load
+  static constexpr int ROWB = D * ES;         // bytes per row
+  static constexpr int U = (32 / RPL) < 8 ? (32 / RPL) : 8;  // loads in flight
+};
+
+__device__ __forceinline__ uint4 ld16(const char* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void unpack(const uint4& v, float (&x)[4]) {
+  x[0] = __uint_as_float(v.x);
+  x[1] = __uint_as_float(v.y);
+  x[2] = __uint_as_float(v.z);
+  x[3] = __uint_as_float(v.w);
+}
+
+__device__ __forceinline__ void unpack(const uint4& v, float (&x)[8]) {
+  x[0] = __uint_as_float(v.x << 16);
+  x[1] = __uint_as_float(v.x & 0xffff0000u);
+  x[2] = __uint_as_float(v.y << 16);
+  x[3] = __uint_as_float(v.y & 0xffff0000u);
+  x[4] = __uint_as_float(v.z << 16);
+  x[5] = __uint_as_float(v.z & 0xffff0000u);
+  x[6] = __uint_as_float(v.w << 16);
+  x[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Cross-lane moves inside a row of 16 lanes with DPP (register to register,
+// no LDS round trip).  After xor-1 and xor-2 quad permutes every lane of a
+// quad holds the quad's value; the half-row mirror (lane i <- 7 - i) then
+// pairs the two quads of each half row, and the row mirror (i <- 15 - i) the
+// two halves, so the four steps reduce 2, 4, 8 and 16 lanes.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x) {
+  const long long u = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xffffffffll), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Sum over groups of N lanes (N = 2 .. 32, aligned); every lane of a group
+// gets the group's sum.
+template <int N, typename T>
+__device__ __forceinline__ T group_sum(T x) {
+  if constexpr (N > 1) x += dpp<kDppXor1>(x);
+  if constexpr (N > 2) x += dpp<kDppXor2>(x);
+  if constexpr (N > 4) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N > 8) x += dpp<kDppMirror>(x);
+  if constexpr (N > 16) x += __shfl_xor(x, 16);
+  return x;
+}
+
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  return group_sum<LPR>(x);
+}
+
+// Sum of an int over the 64 lanes of a wave, returned to every lane.
+__device__ __forceinline__ int wave_sum(int x) {
+  x = group_sum<16>(x);
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
+}
+
+// Exclusive prefix over the lanes of a wave of a small non-negative count
+// (< 32), from one ballot per bit: no LDS round trip.
+__device__ __forceinline__ int wave_prefix_small(int c) {
+  int base = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {
+    const uint64_t m = __ballot((c >> bit) & 1);
+    base += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << bit;
+  }
+  return base;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+__device__ __forceinline__ double readlane_d(double x, int lane) {
+  const long long u = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane((int)(u & 0xffffffffll), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(u >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Maximum over the 64 lanes of a wave, returned to every lane.
+template <typename T>
+__device__ __forceinline__ T wave_max(T x) {
+  T y = dpp<kDppXor1>(x);
+  x = y > x ? y : x;
+  y = dpp<kDppXor2>(x);
+  x = y > x ? y : x;
+  y = dpp<kDppHalfMirror>(x);
+  x = y > x ? y : x;
+  y = dpp<kDppMirror>(x);
+  x = y > x ? y : x;
+  T r = x;
+#pragma unroll
+  for (int row = 1; row < 4; ++row) {
+    T v;
+    if constexpr (sizeof(T) == 4) {
+      v = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16 * row));
+    }
+    r = v > r ? v : r;
+  }
+  if constexpr (sizeof(T) == 4) r = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), 0));
+  return r;
+}
+
+// Online-softmax state of one lane: running max m (base-2 logits), running
+// sum l and the partial output of the lane's E dimensions.
+template <int E>
+struct State {
+  float m, l, acc[E];
+  __device__ __forceinline__ void init() {
+    m = kFloor;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  }
+};
+
+// Attend over `nrows` consecutive rows starting at K / V (already offset to
+// the lane's chunk).  q holds the lane's chunk of scale*log2(e)*q; bias2 is
+// the additive logit bias of these rows in base 2.  Lanes of row group `grp`
+// take rows grp, grp + RPL, ...
+// Row `srow` (if in range) is read from sK / sV instead of K / V.  Rows in
+// [nvalid, nrows) are read (they must be addressable) but carry no weight:
+// this lets a caller issue loads before it knows how many rows count.  U =
+// row loads of K and of V in flight per lane.
+template <int DT, int D, int U = Geo<DT, D>::U>
+__device__ __forceinline__ void attend_range(const char* __restrict__ K, const char* __restrict__ V,
+                                             int nrows, float bias2,
+                                             const float (&q)[Geo<DT, D>::E],
+                                             State<Geo<DT, D>::E>& st, int grp, int srow = -1,
+                                             const char* sK = nullptr, const char* sV = nullptr,
+                                             int nvalid = 1 << 30) {
+  using G = Geo<DT, D>;
+  constexpr int E = G::E;
+  const int nv = min(nvalid, nrows);
+  for (int r0 = 0; r0 < nrows; r0 += G::RPL * U) {
+    uint4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + u * G::RPL + grp;
+      if (row < nrows) {
+        const bool sp = row == srow;
+        kr[u] = ld16(sp ? sK : K + (size_t)row * G::ROWB);
+        vr[u] = ld16(sp ? sV : V + (size_t)row * G::ROWB);
+      } else {
+        kr[u] = make_uint4(0u, 0u, 0u, 0u);
+        vr[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    float s[U];
+    float mt = kFloor;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float k[E];
+      unpack(kr[u], k);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) d = fmaf(q[e], k[e], d);
+      d = row_sum<G::LPR>(d);
+      const bool valid = r0 + u * G::RPL + grp < nv;
+      s[u] = valid ? d + bias2 : -INFINITY;
+      if (!valid) vr[u] = make_uint4(0u, 0u, 0u, 0u);  // weight 0 must not meet a NaN
+      mt = fmaxf(mt, s[u]);
+    }
+    const float mn = fmaxf(st.m, mt);
+    const float alpha = fexp2(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = fexp2(s[u] - mn);
+      st.l += p;
+      float v[E];
+      unpack(vr[u], v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[e] = fmaf(p, v[e], st.acc[e]);
+    }
+    st.m = mn;
+  }
+}
+
+// Merge the RPL row groups of a wave: afterwards every lane holds the wave's
+// state for its chunk.
+template <int LPR, int E>
+__device__ __forceinline__ void merge_groups(State<E>& st) {
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    const float mo = __shfl_xor(st.m, off);
+    const float lo = __shfl_xor(st.l, off);
+    const float mn = fmaxf(st.m, mo);
+    const float a = fexp2(st.m - mn), b = fexp2(mo - mn);
+    st.l = st.l * a + lo * b;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float ao = __shfl_xor(st.acc[e], off);
+      st.acc[e] = st.acc[e] * a + ao * b;
+    }
+    st.m = mn;
+  }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void load_q(const void* q, int unit, int c, float scale,
+                                       float (&x)[Geo<DT, D>::E]) {
+  using G = Geo<DT, D>;
+  const uint4 v = ld16(static_cast<const char*>(q) + (size_t)unit * G::ROWB + c * 16);
+  unpack(v, x);
+#pragma unroll
+  for (int e = 0; e < G::E; ++e) x[e] *= scale;
+}
+
+// Store E output values (already normalised) of chunk c of `unit`.
+template <int DT, int D>
+__device__ __forceinline__ void store_chunk(void* out, int unit, int c, const float* o) {
+  using G = Geo<DT, D>;
+  char* p = static_cast<char*>(out) + (size_t)unit * G::ROWB + c * 16;
+  if constexpr (DT == 0) {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  } else {
+    uint4 w;
+    w.x = bf16_bits(o[0]) | (bf16_bits(o[1]) << 16);
+    w.y = bf16_bits(o[2]) | (bf16_bits(o[3]) << 16);
+    w.z = bf16_bits(o[4]) | (bf16_bits(o[5]) << 16);
+    w.w = bf16_bits(o[6]) | (bf16_bits(o[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+}
+
+// End of a workgroup's work: the W waves merge their states through LDS.
+// With one split per unit wave 0 normalises and writes the output; otherwise
+// it leaves the workgroup's (max, sum, partial output) in the workspace for
+// k_split_merge, which runs after this kernel in the same stream (the kernel
+// boundary makes the partials visible; no device-wide fence or atomic is
+// needed).
+constexpr int kMaxWaves = 16;
+
+template <int DT, int D>
+__device__ __forceinline__ void wg_finish(State<Geo<DT, D>::E>& st, float (*lds_ml)[2], float* lds_o,
+                                          const DecodeArgs& a, int unit, int split) {
+  using G = Geo<DT, D>;
+  constexpr int E = G::E;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int grp = lane / G::LPR, c = lane % G::LPR;
+  merge_groups<G::LPR, E>(st);
+  if (grp == 0) {
+    float4* dst = reinterpret_cast<float4*>(lds_o + wave * D + c * E);
+#pragma unroll
+    for (int e = 0; e < E; e += 4) dst[e / 4] = make_float4(st.acc[e], st.acc[e + 1], st.acc[e + 2], st.acc[e + 3]);
+  }
+  if (lane == 0) {
+    lds_ml[wave][0] = st.m;
+    lds_ml[wave][1] = st.l;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  constexpr int DPL = D / 64;  // dimensions per lane in the merge
+  float M = kFloor;
+  for (int w = 0; w < W; ++w) M = fmaxf(M, lds_ml[w][0]);
+  float L = 0.f, O[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) O[i] = 0.f;
+  for (int w = 0; w < W; ++w) {
+    const float l = lds_ml[w][1];
+    if (l == 0.f) continue;
+    const float f = fexp2(lds_ml[w][0] - M);
+    L = fmaf(f, l, L);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) O[i] = fmaf(f, lds_o[w * D + lane * DPL + i], O[i]);
+  }
+  if (a.splits == 1) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    char* dst = static_cast<char*>(a.out) + (size_t)unit * G::ROWB;
+    if constexpr (DT == 0) {
+      float* d = reinterpret_cast<float*>(dst) + lane * DPL;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) d[i] = O[i] * inv;
+    } else {
+      uint16_t* d = reinterpret_cast<uint16_t*>(dst) + lane * DPL;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) d[i] = (uint16_t)bf16_bits(O[i] * inv);
+    }
+    return;
+  }
+  const size_t part = (size_t)unit * a.splits + split;
+  if (lane == 0) *reinterpret_cast<float2*>(a.part_ml + part * 2) = make_float2(M, L);
+  float* po = a.part_o + part * D + lane * DPL;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) po[i] = O[i];
+}
+
+// ---------------------------------------------------------------------------
+// uocr_ring_append: one workgroup per sequence
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(256) void k_ring_append(AppendArgs a) {
+  using G = Geo<DT, D>;
+  const int b = blockIdx.x;
+  __shared__ int slot_s;
+  int t = 0;
+  if (threadIdx.x == 0) {
+    t = max(a.t_gen[b], 0);
+    slot_s = t % a.window;
+  }
+  __syncthreads();
+  const int slot = slot_s;
+  constexpr int CPR = G::ROWB / 16;  // 16-byte chunks per row
+  const int per = a.heads * CPR;
+  for (int i = threadIdx.x; i < 2 * per; i += blockDim.x) {
+    const int which = i / per, ci = i - which * per;
+    const int h = ci / CPR, off = ci - h * CPR;
+    const size_t unit = (size_t)b * a.heads + h;
+    const char* src = static_cast<const char*>(which ? a.v_new : a.k_new) + unit * G::ROWB + off * 16;
+    char* dst = static_cast<char*>(which ? a.v_ring : a.k_ring) +
+                (unit * a.window + slot) * G::ROWB + off * 16;
+    *reinterpret_cast<uint4*>(dst) = ld16(src);
+  }
+  if (threadIdx.x == 0) a.t_gen[b] = t + 1;
+}
+
+// ---------------------------------------------------------------------------
+// uocr_rswa_decode: dense prefix + window.  One workgroup per (unit, split);
+// its W waves take contiguous slices of the split's keys.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(1024) void k_rswa_decode(DecodeArgs a) {
+  using G = Geo<DT, D>;
+  __shared__ float lds_ml[kMaxWaves][2];
+  __shared__ __attribute__((aligned(16))) float lds_o[kMaxWaves * D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int unit = blockIdx.x / a.splits, split = blockIdx.x - unit * a.splits;
+  const int b = unit / a.heads;
+  const int m = min(max(a.prefix_len[b], 0), a.prefix_cap);
+  const int w = min(max(a.t_gen[b], 0), a.window);
+  // virtual key index: [0, m) prefix rows, [m, m + w) ring slots 0 .. w-1
+  const int lo = split * a.chunk, hi = min(lo + a.chunk, m + w);
+  const int per = hi > lo ? (hi - lo + W - 1) / W : 0;
+  const int wlo = lo + wave * per, whi = min(wlo + per, hi);
+  const int grp = lane / G::LPR, c = lane % G::LPR;
+
+  float q[G::E];
+  load_q<DT, D>(a.q, unit, c, a.qscale, q);
+  State<G::E> st;
+  st.init();
+  const size_t cb = (size_t)c * 16;
+  if (wlo < min(whi, m)) {
+    const size_t base = ((size_t)unit * a.prefix_cap + wlo) * G::ROWB + cb;
+    attend_range<DT, D>(static_cast<const char*>(a.k_prefix) + base,
+                        static_cast<const char*>(a.v_prefix) + base, min(whi, m) - wlo, 0.f, q, st, grp);
+  }
+  const int w0 = max(wlo, m) - m, w1 = whi - m;
+  if (w0 < w1) {
+    const size_t base = ((size_t)unit * a.window + w0) * G::ROWB + cb;
+    attend_range<DT, D>(static_cast<const char*>(a.k_ring) + base,
+                        static_cast<const char*>(a.v_ring) + base, w1 - w0, 0.f, q, st, grp);
+  }
+  wg_finish<DT, D>(st, lds_ml, lds_o, a, unit, split);
+}
+
+// Merge of the splits of every unit: one wave per unit.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void k_split_merge(DecodeArgs a) {
+  using G = Geo<DT, D>;
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= a.units) return;
+  const int S = a.splits;
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)unit * S;
+  float M = kFloor;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s].x);
+  float L = 0.f, O[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) O[i] = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float2 v = ml[s];
+    if (v.y == 0.f) continue;
+    const float f = fexp2(v.x - M);
+    L = fmaf(f, v.y, L);
+    const float* src = a.part_o + ((size_t)unit * S + s) * D + lane * DPL;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) O[i] = fmaf(f, src[i], O[i]);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  char* dst = static_cast<char*>(a.out) + (size_t)unit * G::ROWB;
+  if constexpr (DT == 0) {
+    float* d = reinterpret_cast<float*>(dst) + lane * DPL;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) d[i] = O[i] * inv;
+  } else {
+    uint16_t* d = reinterpret_cast<uint16_t*>(dst) + lane * DPL;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) d[i] = (uint16_t)bf16_bits(O[i] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// uocr_srswa_decode: one workgroup per unit; tasks = live selected blocks +
+// 32-row window chunks, dealt round-robin to the W waves.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(512) void k_srswa_decode(DecodeArgs a) {
+  using G = Geo<DT, D>;
+  __shared__ float lds_ml[kMaxWaves][2];
+  __shared__ __attribute__((aligned(16))) float lds_o[kMaxWaves * D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int unit = blockIdx.x;
+  const int b = unit / a.heads;
+  const int m = min(max(a.prefix_len[b], 0), a.prefix_cap);
+  const int w = min(max(a.t_gen[b], 0), a.window);
+  const int nb = (m + kBlock - 1) / kBlock;
+
+  // Selection entries of this unit, one per lane; a block is live when its
+  // index is in range and its weight is non-zero (bias > -inf).
+  int idx = -1;
+  float bias = 0.f;
+  bool live = false;
+  if (lane < a.topk) {
+    idx = a.sel_idx[(size_t)unit * a.topk + lane];
+    bias = a.sel_bias ? a.sel_bias[(size_t)unit * a.topk + lane] : 0.f;
+    live = idx >= 0 && idx < nb && bias > -INFINITY;
+  }
+  const uint64_t mask = __ballot(live);
+  const int n_live = __popcll(mask);
+  const int n_tasks = n_live + (w + kBlock - 1) / kBlock;
+  const int grp = lane / G::LPR, c = lane % G::LPR;
+
+  float q[G::E];
+  load_q<DT, D>(a.q, unit, c, a.qscale, q);
+  State<G::E> st;
+  st.init();
+  const size_t cb = (size_t)c * 16;
+  for (int t = wave; t < n_tasks; t += W) {
+    if (t < n_live) {
+      uint64_t mm = mask;
+      for (int i = 0; i < t; ++i) mm &= mm - 1;  // drop the t lowest live entries
+      const int slot = __ffsll((unsigned long long)mm) - 1;
+      const int j = __shfl(idx, slot);
+      const float bj = __shfl(bias, slot);
+      const int r0 = j * kBlock;
+      const size_t base = ((size_t)unit * a.prefix_cap + r0) * G::ROWB + cb;
+      attend_range<DT, D>(static_cast<const char*>(a.k_prefix) + base,
+                          static_cast<const char*>(a.v_prefix) + base, min(kBlock, m - r0),
+                          bj * kLog2e, q, st, grp);
+    } else {
+      const int r0 = (t - n_live) * kBlock;
+      const size_t base = ((size_t)unit * a.window + r0) * G::ROWB + cb;
+      attend_range<DT, D>(static_cast<const char*>(a.k_ring) + base,
+                          static_cast<const char*>(a.v_ring) + base, min(kBlock, w - r0), 0.f, q, st,
+                          grp);
+    }
+  }
+  wg_finish<DT, D>(st, lds_ml, lds_o, a, unit, 0);
+}
+
+// ---------------------------------------------------------------------------
+// uocr_block_index_build: one wave per (unit, block); fp64 accumulation
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(256) void k_block_index(IndexArgs a) {
+  using G = Geo<DT, D>;
+  constexpr int E = G::E;
+  __shared__ float Ps[D * kIdxDim];
+  for (int i = threadIdx.x; i < D * kIdxDim; i += blockDim.x) Ps[i] = a.proj[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int grp = lane / G::LPR, c = lane % G::LPR;
+  const size_t total = (size_t)a.units * a.nb_cap;
+  for (size_t item = (size_t)blockIdx.x * kWaves + (threadIdx.x >> 6); item < total;
+       item += (size_t)gridDim.x * kWaves) {
+    const int unit = (int)(item / a.nb_cap), j = (int)(item - (size_t)unit * a.nb_cap);
+    const int b = unit / a.heads;
+    const int m = min(max(a.prefix_len[b], 0), a.prefix_cap);
+    float* dst = a.kbar + item * kIdxDim;
+    if (j * kBlock >= m) {
+      if (lane < kIdxDim) dst[lane] = 0.f;
+      continue;
+    }
+    const int r0 = j * kBlock, nr = min(kBlock, m - r0);
+    const char* K = static_cast<const char*>(a.k_prefix) + ((size_t)unit * a.prefix_cap + r0) * G::ROWB + c * 16;
+    double sum[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) sum[e] = 0.0;
+#pragma unroll 4
+    for (int r = grp; r < nr; r += G::RPL) {
+      float x[E];
+      unpack(ld16(K + (size_t)r * G::ROWB), x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) sum[e] += (double)x[e];
+    }
+#pragma unroll
+    for (int off = G::LPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < E; ++e) sum[e] += __shfl_xor(sum[e], off);
+    // every lane now holds the block sums of dims c*E .. c*E+E-1; row group
+    // grp produces outputs grp, grp + RPL, ...
+    const double inv = 1.0 / (double)nr;
+    for (int i = grp; i < kIdxDim; i += G::RPL) {
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc += (double)Ps[(c * E + e) * kIdxDim + i] * (sum[e] * inv);
+      acc = group_sum<G::LPR>(acc);
+      if (c == 0) dst[i] = (float)acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// uocr_block_score: `parts` workgroups per unit; fp64 accumulation
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(256) void k_block_score(ScoreArgs a) {
+  using G = Geo<DT, D>;
+  __shared__ double red[8][kIdxDim];
+  __shared__ double qidx[kIdxDim];
+  const int unit = blockIdx.x / a.parts, part = blockIdx.x - unit * a.parts;
+  const int tid = threadIdx.x;
+  {
+    // q_idx = P^T q: thread (i = tid % 32, slice = tid / 32) sums D/8 dims
+    const int i = tid % kIdxDim, sl = tid / kIdxDim;
+    const char* qrow = static_cast<const char*>(a.q) + (size_t)unit * G::ROWB;
+    double acc = 0.0;
+    for (int d = sl * (D / 8); d < (sl + 1) * (D / 8); ++d) {
+      float qd;
+      if constexpr (DT == 0)
+        qd = reinterpret_cast<const float*>(qrow)[d];
+      else
+        qd = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[d] << 16);
+      acc += (double)a.proj[d * kIdxDim + i] * (double)qd;
+    }
+    red[sl][i] = acc;
+  }
+  __syncthreads();
+  if (tid < kIdxDim) {
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += red[k][tid];
+    qidx[tid] = s;
+  }
+  __syncthreads();
+  const int b = unit / a.heads;
+  const int m = min(max(a.prefix_len[b], 0), a.prefix_cap);
+  const int nb = (m + kBlock - 1) / kBlock;
+  const int per = (a.nb_cap + a.parts - 1) / a.parts;
+  const int j0 = part * per, j1 = min(j0 + per, a.nb_cap);
+  // 8 lanes per block row (32 fp32 = 128 B), 32 rows per workgroup pass
+  const int r = tid / 8, c = tid % 8;
+  double qv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qv[e] = qidx[c * 4 + e];
+  const float* K = a.kbar + (size_t)unit * a.nb_cap * kIdxDim + c * 4;
+  float* out = a.scores + (size_t)unit * a.nb_cap;
+  constexpr int UNR = 4;
+  for (int jb = j0; jb < j1; jb += 32 * UNR) {
+    float4 kv[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int j = jb + u * 32 + r;
+      kv[u] = (j < j1 && j < nb) ? *reinterpret_cast<const float4*>(K + (size_t)j * kIdxDim)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int j = jb + u * 32 + r;
+      double s = qv[0] * (double)kv[u].x + qv[1] * (double)kv[u].y + qv[2] * (double)kv[u].z +
+                 qv[3] * (double)kv[u].w;
+      s = group_sum<8>(s);
+      if (c == 0 && j < j1) out[j] = j < nb ? (float)s : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1.5-entmax + top-k of one unit, computed by the NT threads of a workgroup
+// ---------------------------------------------------------------------------
+constexpr int kSmallCand = 256;
+
+// Order-preserving map of a float to uint32 (larger float, larger key).
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kPairMax = 256;  // largest candidate set ranked pairwise
+constexpr int kWaveBlocks = 16; // blocks per lane on the one-wave path (nb <= 1024)
+
+template <int NT>
+struct __attribute__((aligned(16))) TopkSmem {
+  uint32_t hist[256];
+  int sh_i[NT / 64];
+  float sh_f[NT / 64];
+  double sh_d[NT / 64];
+  uint32_t digit, above;
+  double tau;
+  union alignas(16) {
+    double cand[kMaxBlocks];  // sorted path
+    struct {                  // pairwise path (16-byte aligned rows)
+      float val[kPairMax + 4];
+      int idx[kPairMax + 4];
+      int rank[kPairMax + 4];
+    } a;
+  };
+};
+
+// Exclusive scan of one value per thread over the workgroup; returns the
+// prefix and sets `total`.
+template <int NT, typename T>
+__device__ __forceinline__ T block_scan_excl(T x, T& total, T* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  T inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  T base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const T v = sh[w];
+    if (w < wave) base += v;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return base + inc - x;
+}
+
+template <int NT, typename T>
+__device__ __forceinline__ T block_max(T x, T* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_max(x);
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  T r = sh[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r = sh[w] > r ? sh[w] : r;
+  __syncthreads();
+  return r;
+}
+
+// Routing of one unit from its nb scores `s` (global or LDS).  Writes topk
+// entries of o_idx / o_prob (may be null) / o_bias and, when l_idx is not
+// null, the same indices and biases to l_idx / l_bias.  Every thread of the
+// workgroup must call it.
+template <int NT>
+__device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int topk, int32_t* o_idx, float* o_prob,
+                                  float* o_bias, int* l_idx, float* l_bias, TopkSmem<NT>& sm) {
+  constexpr int PT = kMaxBlocks / NT;  // values per thread
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kk = min(topk, nb);
+  for (int i = kk + tid; i < topk; i += NT) {
+    o_idx[i] = -1;
+    if (o_prob) o_prob[i] = 0.f;
+    o_bias[i] = -INFINITY;
+    if (l_idx) {
+      l_idx[i] = -1;
+      l_bias[i] = -INFINITY;
+    }
+  }
+  if (kk == 0) return;
+
+  // ---- one-wave path (nb <= 1024 and a candidate set of <= 64 blocks) ----
+  // Wave 0 alone: no workgroup barrier until the end.  Lane l owns blocks
+  // [16 l, 16 l + 16).  With d = smax - s in fp32 (monotone in s), the set
+  // A = {d < T}, T = 4, 8, 16, ... until it holds kk blocks, contains the top
+  // kk (ties of the kk-th included) and the entmax support (exact d < 2 gives
+  // fp32 d <= 2 < 4).  A is compacted in index order, one block per lane; a
+  // broadcast loop over A gives each lane its rank, and one over the entmax
+  // candidates (exact d < 2, compacted first) the prefix statistics of the
+  // sorted order at the end of each candidate's tie group.
+  if (nb <= 64 * kWaveBlocks) {
+    if (wave == 0) {
+      float sv[kWaveBlocks];
+      float lmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < kWaveBlocks; ++e) {
+        const int j = lane * kWaveBlocks + e;
+        sv[e] = j < nb ? s[j] : -INFINITY;
+        lmax = fmaxf(lmax, sv[e]);
+      }
+      const float smax = wave_max(lmax);
+      const double dmax = (double)smax;
+      float dv[kWaveBlocks];
+#pragma unroll
+      for (int e = 0; e < kWaveBlocks; ++e) dv[e] = smax - sv[e];  // +inf past nb
+      float T = 4.f;
+      int nA = 0;
+      for (int it = 0; it < 130; ++it) {
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < kWaveBlocks; ++e) c += dv[e] < T ? 1 : 0;
+        nA = wave_sum(c);
+        if (nA >= kk) break;
+        T = T * 2.f;  // reaches +inf, where every finite d counts
+      }
+      if (nA <= 64) {
+        int c = 0, cc = 0;
+#pragma unroll
+        for (int e = 0; e < kWaveBlocks; ++e) {
+          c += dv[e] < T ? 1 : 0;
+          cc += ((double)sv[e] - dmax) * 0.5 > -1.0 ? 1 : 0;
+        }
+        int pos = wave_prefix_small(c);
+        int cpos = wave_prefix_small(cc);
+        const int nC = wave_sum(cc);
+#pragma unroll
+        for (int e = 0; e < kWaveBlocks; ++e) {
+          if (dv[e] < T) {
+            sm.a.val[pos] = sv[e];
+            sm.a.idx[pos] = lane * kWaveBlocks + e;
+            ++pos;
+          }
+          if (((double)sv[e] - dmax) * 0.5 > -1.0) {
+            sm.a.rank[cpos] = __float_as_int(sv[e]);  // candidate scores
+            ++cpos;
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const bool mine = lane < nA;
+        const float si = mine ? sm.a.val[lane] : -INFINITY;
+        const int ii = mine ? sm.a.idx[lane] : 0x7fffffff;
+        const double vi = ((double)si - dmax) * 0.5;
+        const bool cand = mine && vi > -1.0;
+        int rank = 0;
+        for (int k = 0; k < nA; ++k) {
+          const float sk = readlane_f(si, k);
+          const int ik = __builtin_amdgcn_readlane(ii, k);
+          rank += (sk > si || (sk == si && ik < ii)) ? 1 : 0;
+        }
+        const float ci = lane < nC ? __int_as_float(sm.a.rank[lane]) : -INFINITY;
+        int r = 0;
+        double s1 = 0.0, s2 = 0.0;
+        for (int k = 0; k < nC; ++k) {
+          const float sk = readlane_f(ci, k);
+          if (sk >= si) {
+            const double vk = ((double)sk - dmax) * 0.5;
+            ++r;
+            s1 += vk;
+            s2 += vk * vk;
+          }
+        }
+        int rr = 0;
+        double tl = 0.0;
+        if (cand) {
+          const double mu = s1 / r;
+          const double ss = s2 - s1 * mu;
+          tl = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
+          rr = tl <= vi ? r : 0;
+        }
+        const int rstar = wave_max(rr);
+        const uint64_t win = __ballot(rr == rstar && rr > 0);
+        const double tau = readlane_d(tl, __ffsll((unsigned long long)win) - 1);
+        const bool sel = mine && rank < kk;
+        const uint64_t sm_ = __ballot(sel);
+        if (sel) {
+          const int at = __builtin_amdgcn_mbcnt_hi((uint32_t)(sm_ >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)sm_, 0u));
+          const double dd = vi - tau;
+          const double p = dd > 0.0 ? dd * dd : 0.0;
+          const float bias = p > 0.0 ? (float)log(p) : -INFINITY;
+          o_idx[at] = ii;
+          if (o_prob) o_prob[at] = (float)p;
+          o_bias[at] = bias;
+          if (l_idx) {
+            l_idx[at] = ii;
+            l_bias[at] = bias;
+          }
+        }
+      }
+      if (lane == 0) sm.digit = nA <= 64 ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool done = sm.digit == 1u;
+    __syncthreads();
+    if (done) return;
+  }
+
+  // Thread t owns the contiguous blocks [t*E, t*E + E): index order equals
+  // (thread, position) order, which the ordered compactions below rely on.
+  const int E = (nb + NT - 1) / NT;
+  const int j0 = tid * E;
+  static_assert(PT <= 32, "per-thread flags are 32-bit masks");
+  float v[PT];  // -inf marks a slot past nb; fkey(v) is recomputed when needed
+  uint32_t valid = 0u;
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    const int j = j0 + e;
+    const bool ok = e < E && j < nb;
+    v[e] = ok ? s[j] : -INFINITY;
+    valid |= ok ? (1u << e) : 0u;
+    lmax = fmaxf(lmax, v[e]);
+  }
+  const float smax = block_max<NT, float>(lmax, sm.sh_f);
+  const double dmax = (double)smax;
+
+  // ---- usual case: a small set A holding the top kk and the entmax support ----
+  // Histogram of the binary exponent of d = smax - s (monotone in the
+  // ranking): A = every block whose exponent is at most that of the kk-th
+  // smallest d, and at least that of [2, 4), which holds every d < 2 (the
+  // entmax support) even after fp32 rounding.  Ties of the kk-th score share
+  // its exponent, so A holds them too.
+  for (int i = tid; i < 256; i += NT) sm.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < PT; ++e)
+    if ((valid >> e) & 1u) atomicAdd(&sm.hist[(__float_as_uint(smax - v[e]) >> 23) & 255u], 1u);
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t c0 = sm.hist[4 * lane], c1 = sm.hist[4 * lane + 1], c2 = sm.hist[4 * lane + 2],
+                   c3 = sm.hist[4 * lane + 3];
+    const uint32_t local = c0 + c1 + c2 + c3;
+    uint32_t inc = local;  // inclusive count over lanes <= lane (bins 0 .. 4*lane+3)
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    const uint32_t before = inc - local;
+    const uint32_t cnt[4] = {c0, c1, c2, c3};
+    // smallest bin whose cumulative count reaches kk
+    int estar = 0;
+    uint32_t cum = before;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool first = cum < (uint32_t)kk && cum + cnt[k] >= (uint32_t)kk;
+      estar = first ? 4 * lane + k : estar;
+      cum += cnt[k];
+    }
+    const uint64_t who = __ballot(before < (uint32_t)kk && inc >= (uint32_t)kk);
+    estar = __shfl(estar, __ffsll((unsigned long long)who) - 1);
+    const int efin = estar > 128 ? estar : 128;
+    // |A| = cumulative count through bin efin
+    uint32_t upto = before;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) upto += (4 * lane + k <= efin) ? cnt[k] : 0u;
+    upto = __shfl(upto, efin / 4);
+    if (lane == 0) {
+      sm.digit = (uint32_t)efin;
+      sm.above = upto;
+    }
+  }
+  __syncthreads();
+  const uint32_t efin = sm.digit;
+  const int nA = (int)sm.above;
+  __syncthreads();
+  if (nA <= kPairMax) {
+    uint32_t inA = 0u;
+#pragma unroll
+    for (int e = 0; e < PT; ++e)
+      inA |= (((valid >> e) & 1u) && ((__float_as_uint(smax - v[e]) >> 23) & 255u) <= efin) ? (1u << e) : 0u;
+    int tot;
+    int pos = block_scan_excl<NT, int>(__popc(inA), tot, sm.sh_i);
+#pragma unroll
+    for (int e = 0; e < PT; ++e)
+      if ((inA >> e) & 1u) {
+        sm.a.val[pos] = v[e];
+        sm.a.idx[pos] = j0 + e;
+        ++pos;
+      }
+    // pad to a multiple of 4 with entries that rank below every block
+    const int nA4 = (nA + 3) & ~3;
+    if (tid < nA4 - nA) {
+      sm.a.val[nA + tid] = -INFINITY;
+      sm.a.idx[nA + tid] = 0x7fffffff;
+      sm.a.rank[nA + tid] = 0x7fffffff;
+    }
+    __syncthreads();
+    const float4* val4 = reinterpret_cast<const float4*>(sm.a.val);
+    const int4* idx4 = reinterpret_cast<const int4*>(sm.a.idx);
+    // rank in (score desc, index asc) and, for entmax candidates, the
+    // prefix statistics of the sorted order at the end of the tie group
+    int rbest = 0;
+    double tbest = 0.0;
+    for (int i = tid; i < nA; i += NT) {
+      const float si = sm.a.val[i];
+      const int ii = sm.a.idx[i];
+      const double vi = ((double)si - dmax) * 0.5;
+      const bool cand = vi > -1.0;
+      int rank = 0, r = 0;
+      double s1 = 0.0, s2 = 0.0;
+#pragma unroll 4
+      for (int j4 = 0; j4 < nA4 / 4; ++j4) {
+        const float4 sv = val4[j4];
+        const int4 iv = idx4[j4];
+        const float sj[4] = {sv.x, sv.y, sv.z, sv.w};
+        const int ij[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          rank += (sj[k] > si || (sj[k] == si && ij[k] < ii)) ? 1 : 0;
+          if (cand && sj[k] >= si) {
+            const double vj = ((double)sj[k] - dmax) * 0.5;
+            ++r;
+            s1 += vj;
+            s2 += vj * vj;
+          }
+        }
+      }
+      sm.a.rank[i] = rank;
+      if (cand) {
+        const double mu = s1 / r;
+        const double ss = s2 - s1 * mu;
+        const double tau = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
+        if (tau <= vi && r > rbest) {
+          rbest = r;
+          tbest = tau;
+        }
+      }
+    }
+    const int rstar = block_max<NT, int>(rbest, sm.sh_i);
+    if (rbest == rstar && rbest > 0) sm.tau = tbest;
+    __syncthreads();
+    const double tau = sm.tau;
+    for (int i = tid; i < nA; i += NT) {
+      if (sm.a.rank[i] >= kk) continue;
+      const int ii = sm.a.idx[i];
+      int at = 0;  // output position: selected blocks with a lower index
+      const int4* rank4 = reinterpret_cast<const int4*>(sm.a.rank);
+#pragma unroll 4
+      for (int j4 = 0; j4 < nA4 / 4; ++j4) {
+        const int4 rv = rank4[j4];
+        const int4 iv = idx4[j4];
+        at += (rv.x < kk && iv.x < ii) + (rv.y < kk && iv.y < ii) + (rv.z < kk && iv.z < ii) +
+              (rv.w < kk && iv.w < ii);
+      }
+      const double dd = ((double)sm.a.val[i] - dmax) * 0.5 - tau;
+      const double p = dd > 0.0 ? dd * dd : 0.0;
+      const float bias = p > 0.0 ? (float)log(p) : -INFINITY;
+      o_idx[at] = ii;
+      if (o_prob) o_prob[at] = (float)p;
+      o_bias[at] = bias;
+      if (l_idx) {
+        l_idx[at] = ii;
+        l_bias[at] = bias;
+      }
+    }
+    return;
+  }
+
+  // ---- general case: radix select of the kk-th key, sorted entmax ----
+  uint32_t prefix = 0u, pmask = 0u;
+  int rem = kk;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) sm.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PT; ++e) {
+      const uint32_t key = fkey(v[e]);
+      if (((valid >> e) & 1u) && (key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t c0 = sm.hist[4 * lane], c1 = sm.hist[4 * lane + 1], c2 = sm.hist[4 * lane + 2],
+                     c3 = sm.hist[4 * lane + 3];
+      const uint32_t local = c0 + c1 + c2 + c3;
+      uint32_t inc = local;  // sum over lanes >= lane
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(inc, off);
+        if (lane + off < 64) inc += y;
+      }
+      uint32_t above = inc - local;  // counts strictly above this lane's bins
+      const uint32_t cnt[4] = {c0, c1, c2, c3};
+#pragma unroll
+      for (int k = 3; k >= 0; --k) {
+        if (above < (uint32_t)rem && (uint32_t)rem <= above + cnt[k]) {
+          sm.digit = (uint32_t)(4 * lane + k);
+          sm.above = above;
+        }
+        above += cnt[k];
+      }
+    }
+    __syncthreads();
+    prefix |= sm.digit << shift;
+    pmask |= 255u << shift;
+    rem -= (int)sm.above;
+  }
+  // prefix = key of the kk-th ranked block; take every key above it and the
+  // `rem` lowest-index blocks whose key equals it.
+  int ties = 0;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) ties += (((valid >> e) & 1u) && fkey(v[e]) == prefix) ? 1 : 0;
+  int tie_tot;
+  int tie_before = block_scan_excl<NT, int>(ties, tie_tot, sm.sh_i);
+  uint32_t sel = 0u;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    if (!((valid >> e) & 1u)) continue;
+    const uint32_t key = fkey(v[e]);
+    bool take = key > prefix;
+    if (key == prefix) take = tie_before++ < rem;
+    sel |= take ? (1u << e) : 0u;
+  }
+  const int nsel = __popc(sel);
+
+  // ---- 1.5-entmax threshold, fp64 ----
+  // With u = s/2 the threshold satisfies tau >= max(u) - 1, so only blocks
+  // with s > max(s) - 2 can carry weight.  v = (s - smax)/2 lies in (-1, 0].
+  uint32_t cmask = 0u;
+#pragma unroll
+  for (int e = 0; e < PT; ++e)
+    cmask |= (((valid >> e) & 1u) && ((double)v[e] - dmax) * 0.5 > -1.0) ? (1u << e) : 0u;
+  int C;
+  int cpos = block_scan_excl<NT, int>(__popc(cmask), C, sm.sh_i);
+#pragma unroll
+  for (int e = 0; e < PT; ++e)
+    if ((cmask >> e) & 1u) sm.cand[cpos++] = ((double)v[e] - dmax) * 0.5;
+  __syncthreads();
+
+  int rbest = 0;
+  double tbest = 0.0;
+  if (C <= kSmallCand) {
+    // r_i = #{v_j >= v_i}: the last position of v_i's tie group in the
+    // descending order; the prefix condition is checked there.
+    if (tid < C) {
+      const double vi = sm.cand[tid];
+      int r = 0;
+      double s1 = 0.0, s2 = 0.0;
+      for (int j = 0; j < C; ++j) {
+        const double vj = sm.cand[j];
+        if (vj >= vi) {
+          ++r;
+          s1 += vj;
+          s2 += vj * vj;
+        }
+      }
+      const double mu = s1 / r;
+      const double ss = s2 - s1 * mu;
+      const double tau = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
+      if (tau <= vi) {
+        rbest = r;
+        tbest = tau;
+      }
+    }
+  } else {
+    // Many candidates: bitonic sort (descending) in LDS, then prefix sums.
+    int P = 1;
+    while (P < C) P <<= 1;
+    for (int i = C + tid; i < P; i += NT) sm.cand[i] = -INFINITY;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < P / 2; i += NT) {
+          const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+          const bool desc = (lo & size) == 0;
+          const double x = sm.cand[lo], y = sm.cand[hi];
+          if ((x < y) == desc) {
+            sm.cand[lo] = y;
+            sm.cand[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    const int per = (P + NT - 1) / NT;
+    const int p0 = tid * per;
+    double l1 = 0.0, l2 = 0.0;
+    for (int i = 0; i < per && p0 + i < C; ++i) {
+      const double x = sm.cand[p0 + i];
+      l1 += x;
+      l2 += x * x;
+    }
+    double t1, t2;
+    double s1 = block_scan_excl<NT, double>(l1, t1, sm.sh_d);
+    double s2 = block_scan_excl<NT, double>(l2, t2, sm.sh_d);
+    for (int i = 0; i < per && p0 + i < C; ++i) {
+      const double x = sm.cand[p0 + i];
+      s1 += x;
+      s2 += x * x;
+      const int r = p0 + i + 1;
+      const double mu = s1 / r;
+      const double ss = s2 - s1 * mu;
+      const double tau = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
+      if (tau <= x) {
+        rbest = r;
+        tbest = tau;
+      }
+    }
+  }
+  const int rstar = block_max<NT, int>(rbest, sm.sh_i);
+  if (rbest == rstar && rbest > 0) sm.tau = tbest;  // equal r gives the same tau
+  __syncthreads();
+  const double tau = sm.tau;
+
+  // ---- outputs in ascending index order ----
+  int stot;
+  int pos = block_scan_excl<NT, int>(nsel, stot, sm.sh_i);
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    if (!((sel >> e) & 1u)) continue;
+    const double d = ((double)v[e] - dmax) * 0.5 - tau;
+    const double p = d > 0.0 ? d * d : 0.0;
+    const float bias = p > 0.0 ? (float)log(p) : -INFINITY;
+    o_idx[pos] = j0 + e;
+    if (o_prob) o_prob[pos] = (float)p;
+    o_bias[pos] = bias;
+    if (l_idx) {
+      l_idx[pos] = j0 + e;
+      l_bias[pos] = bias;
+    }
+    ++pos;
+  }
+}
+
+constexpr int kTopkThreads = 256;
+
+__global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
+  __shared__ TopkSmem<kTopkThreads> sm;
+  const int unit = blockIdx.x;
+  const int b = unit / a.heads;
+  const int m = min(max(a.prefix_len[b], 0), a.prefix_cap);
+  const int nb = min((m + kBlock - 1) / kBlock, a.nb_cap);
+  const size_t o = (size_t)unit * a.topk;
+  entmax_topk_block<kTopkThreads>(a.scores + (size_t)unit * a.nb_cap, nb, a.topk, a.sel_idx + o,
+                                  a.sel_prob ? a.sel_prob + o : nullptr, a.sel_bias + o, nullptr, nullptr, sm);
+}
+
+// ---------------------------------------------------------------------------
+// Fused steps: append + (route +) decode in one launch
+// ---------------------------------------------------------------------------
+// uocr_srswa_step: one workgroup of NT threads per unit runs the whole step.
+// The window does not depend on the routing, so it is attended first, while
+// the block keys are in flight:
+//   1. write the new token into its ring slot; issue the loads of the block
+//      keys; q_idx = P^T q (fp64); attend over the window (the new token's
+//      row is taken from k_new / v_new, so no wave waits for the ring write);
+//   2. block scores into LDS; entmax + top-k in LDS;
+//   3. attend over the live selected blocks; merge the waves through LDS.
+template <int DT, int D, int NT>
+__global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a) {
+  using G = Geo<DT, D>;
+  constexpr int W = NT / 64;
+  constexpr int SL = NT / kIdxDim;  // slices of D in the q_idx product
+  constexpr int KB = 4;             // block keys loaded per thread per batch
+  constexpr int RPP = NT / 8;       // block keys per pass (8 lanes per key)
+  __shared__ float s_scores[kMaxBlocks];
+  __shared__ double s_red[SL][kIdxDim];
+  __shared__ double s_qidx[kIdxDim];
+  __shared__ TopkSmem<NT> tsm;
+  __shared__ int l_idx[kMaxTopk];
+  __shared__ float l_bias[kMaxTopk];
+  __shared__ float lds_ml[W][2];
+  __shared__ __attribute__((aligned(16))) float lds_o[W * D];
+  const DecodeArgs& d = a.d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int unit = blockIdx.x, b = unit / d.heads, h = unit - b * d.heads;
+  const int m = min(max(d.prefix_len[b], 0), d.prefix_cap);
+  const int t = max(a.t_gen_in[b], 0);
+  const int n = d.window, slot = t % n, w = min(n, t + 1);
+  const int nb = (m + kBlock - 1) / kBlock;
+  const int grp = lane / G::LPR, c = lane % G::LPR;
+  const size_t cb = (size_t)c * 16;
+
+  // ring append of this unit's row
+  constexpr int CPR = G::ROWB / 16;
+  if (tid < 2 * CPR) {
+    const int which = tid / CPR, off = tid - which * CPR;
+    const char* src = static_cast<const char*>(which ? a.v_new : a.k_new) + (size_t)unit * G::ROWB + off * 16;
+    char* dst = static_cast<char*>(which ? a.v_ring : a.k_ring) + ((size_t)unit * n + slot) * G::ROWB + off * 16;
+    *reinterpret_cast<uint4*>(dst) = ld16(src);
+  }
+  if (h == 0 && tid == 0) a.t_gen_out[b] = t + 1;
+
+  // first two batches of block keys, in flight during the window attention
+  const int kr = tid / 8, kc = tid % 8;
+  const float* K = a.kbar + (size_t)unit * a.nb_cap * kIdxDim + kc * 4;
+  auto load_keys = [&](float4 (&dst)[KB], int jb) {  // rows < nb_cap: no wait for prefix_len
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int j = jb + u * RPP + kr;
+      dst[u] = j < a.nb_cap ? *reinterpret_cast<const float4*>(K + (size_t)j * kIdxDim)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float4 kvA[KB], kvB[KB];
+  load_keys(kvA, 0);
+  load_keys(kvB, RPP * KB);
+
+  // q_idx partial sums
+  {
+    const int i = tid % kIdxDim, sl = tid / kIdxDim;
+    constexpr int DPS = D / SL;
+    const char* qrow = static_cast<const char*>(d.q) + (size_t)unit * G::ROWB;
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < DPS; ++k) {
+      const int dd = sl * DPS + k;
+      float qd;
+      if constexpr (DT == 0)
+        qd = reinterpret_cast<const float*>(qrow)[dd];
+      else
+        qd = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[dd] << 16);
+      acc += (double)a.proj[dd * kIdxDim + i] * (double)qd;
+    }
+    s_red[sl][i] = acc;
+  }
+
+  // window: wave w takes rows [w*WR, w*WR + WR) of the visible window
+  float q[G::E];
+  load_q<DT, D>(d.q, unit, c, d.qscale, q);
+  State<G::E> st;
+  st.init();
+  {
+    // every slot of the ring is addressable: read this wave's share of all n
+    // slots and let only the first w count
+    const int WR = (n + W - 1) / W;
+    const int r0 = wave * WR, r1 = min(r0 + WR, n);
+    if (r0 < r1) {
+      const size_t base = ((size_t)unit * n + r0) * G::ROWB + cb;
+      const size_t nbase = (size_t)unit * G::ROWB + cb;
+      // a 128-row window over 8 waves is 16 rows per wave: half the loads in flight
+      constexpr int UW = (G::U / 2) > 0 ? G::U / 2 : 1;
+      attend_range<DT, D, UW>(static_cast<const char*>(d.k_ring) + base, static_cast<const char*>(d.v_ring) + base,
+                              r1 - r0, 0.f, q, st, grp, slot - r0, static_cast<const char*>(a.k_new) + nbase,
+                              static_cast<const char*>(a.v_new) + nbase, w - r0);
+    }
+  }
+  __syncthreads();
+  if (tid < kIdxDim) {
+    double sum = 0.0;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) sum += s_red[k][tid];
+    s_qidx[tid] = sum;
+  }
+  __syncthreads();
+
+  // block scores (fp64 dot products, rounded once to fp32) into LDS; the
+  // next batch of keys is loaded while the current one is scored
+  {
+    double qv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[e] = s_qidx[kc * 4 + e];
+    auto score = [&](const float4 (&kv)[KB], int jb) {
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int j = jb + u * RPP + kr;
+        double sc = qv[0] * (double)kv[u].x + qv[1] * (double)kv[u].y + qv[2] * (double)kv[u].z +
+                    qv[3] * (double)kv[u].w;
+        sc = group_sum<8>(sc);
+        if (kc == 0 && j < nb) s_scores[j] = (float)sc;
+      }
+    };
+    constexpr int BATCH = RPP * KB;
+    for (int jb = 0; jb < nb; jb += 2 * BATCH) {
+      score(kvA, jb);
+      if (jb + 2 * BATCH < a.nb_cap) load_keys(kvA, jb + 2 * BATCH);
+      score(kvB, jb + BATCH);
+      if (jb + 3 * BATCH < a.nb_cap) load_keys(kvB, jb + 3 * BATCH);
+    }
+  }
+  __syncthreads();
+
+  const size_t so = (size_t)unit * d.topk;
+  entmax_topk_block<NT>(s_scores, nb, d.topk, a.sel_idx + so, a.sel_prob ? a.sel_prob + so : nullptr,
+                        a.sel_bias + so, l_idx, l_bias, tsm);
+  __syncthreads();
+
+  // live selected blocks, dealt round-robin to the waves
+  int idx = -1;
+  float bias = 0.f;
+  bool live = false;
+  if (lane < d.topk) {
+    idx = l_idx[lane];
+    bias = l_bias[lane];
+    live = idx >= 0 && idx < nb && bias > -INFINITY;
+  }
+  const uint64_t mask = __ballot(live);
+  const int n_live = __popcll(mask);
+  for (int tk = wave; tk < n_live; tk += W) {
+    uint64_t mm = mask;
+    for (int i = 0; i < tk; ++i) mm &= mm - 1;
+    const int sl = __ffsll((unsigned long long)mm) - 1;
+    const int j = __shfl(idx, sl);
+    const float bj = __shfl(bias, sl);
+    const int r0 = j * kBlock;
+    const size_t base = ((size_t)unit * d.prefix_cap + r0) * G::ROWB + cb;
+    attend_range<DT, D>(static_cast<const char*>(d.k_prefix) + base, static_cast<const char*>(d.v_prefix) + base,
+                        min(kBlock, m - r0), bj * kLog2e, q, st, grp);
+  }
+  wg_finish<DT, D>(st, lds_ml, lds_o, d, unit, 0);
+}
+
+// uocr_rswa_step: the dense decode with the append fused in.  Every
+// workgroup reads the new token's row from k_new / v_new instead of the ring
+// slot it goes to; the workgroup of split 0 writes it into the ring.
+template <int DT, int D>
+__global__ __launch_bounds__(1024) void k_rswa_step(StepArgs a) {
+  using G = Geo<DT, D>;
+  __shared__ float lds_ml[kMaxWaves][2];
+  __shared__ __attribute__((aligned(16))) float lds_o[kMaxWaves * D];
+  const DecodeArgs& d = a.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int unit = blockIdx.x / d.splits, split = blockIdx.x - unit * d.splits;
+  const int b = unit / d.heads, h = unit - b * d.heads;
+  const int m = min(max(d.prefix_len[b], 0), d.prefix_cap);
+  const int t = max(a.t_gen_in[b], 0);
+  const int n = d.window, slot = t % n, w = min(n, t + 1);
+  constexpr int CPR = G::ROWB / 16;
+  if (split == 0 && threadIdx.x < 2 * CPR) {
+    const int which = threadIdx.x / CPR, off = threadIdx.x - which * CPR;
+    const char* src = static_cast<const char*>(which ? a.v_new : a.k_new) + (size_t)unit * G::ROWB + off * 16;
+    char* dst = static_cast<char*>(which ? a.v_ring : a.k_ring) + ((size_t)unit * n + slot) * G::ROWB + off * 16;
+    *reinterpret_cast<uint4*>(dst) = ld16(src);
+  }
+  if (split == 0 && h == 0 && threadIdx.x == 0) a.t_gen_out[b] = t + 1;
+
+  const int lo = split * d.chunk, hi = min(lo + d.chunk, m + w);
+  const int per = hi > lo ? (hi - lo + W - 1) / W : 0;
+  const int wlo = lo + wave * per, whi = min(wlo + per, hi);
+  const int grp = lane / G::LPR, c = lane % G::LPR;
+  float q[G::E];
+  load_q<DT, D>(d.q, unit, c, d.qscale, q);
+  State<G::E> st;
+  st.init();
+  const size_t cb = (size_t)c * 16;
+  if (wlo < min(whi, m)) {
+    const size_t base = ((size_t)unit * d.prefix_cap + wlo) * G::ROWB + cb;
+    attend_range<DT, D>(static_cast<const char*>(d.k_prefix) + base,
+                        static_cast<const char*>(d.v_prefix) + base, min(whi, m) - wlo, 0.f, q, st, grp);
+  }
+  const int w0 = max(wlo, m) - m, w1 = whi - m;
+  if (w0 < w1) {
+    const size_t base = ((size_t)unit * n + w0) * G::ROWB + cb;
+    const size_t nb_ = (size_t)unit * G::ROWB + cb;
+    attend_range<DT, D>(static_cast<const char*>(d.k_ring) + base, static_cast<const char*>(d.v_ring) + base,
+                        w1 - w0, 0.f, q, st, grp, slot - w0, static_cast<const char*>(a.k_new) + nb_,
+                        static_cast<const char*>(a.v_new) + nb_);
+  }
+  wg_finish<DT, D>(st, lds_ml, lds_o, d, unit, split);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+#define UOCR_DISPATCH(KERNEL, GRID, BLOCK, ARGS)                                   \
+  do {                                                                              \
+    if (dtype == 0 && head_dim == 64) KERNEL<0, 64><<<GRID, BLOCK, 0, s>>>(ARGS);   \
+    else if (dtype == 0 && head_dim == 128) KERNEL<0, 128><<<GRID, BLOCK, 0, s>>>(ARGS); \
+    else if (dtype == 1 && head_dim == 64) KERNEL<1, 64><<<GRID, BLOCK, 0, s>>>(ARGS);   \
+    else if (dtype == 1 && head_dim == 128) KERNEL<1, 128><<<GRID, BLOCK, 0, s>>>(ARGS); \
+    else return hipErrorInvalidValue;                                               \
+  } while (0)
+
+hipError_t launch_ring_append(int dtype, int head_dim, const AppendArgs& a, hipStream_t s) {
+  UOCR_DISPATCH(k_ring_append, dim3(a.batch), dim3(256), a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rswa_decode(int dtype, int head_dim, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((long)a.units * a.splits));
+  UOCR_DISPATCH(k_rswa_decode, grid, dim3(64 * a.waves), a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  UOCR_DISPATCH(k_split_merge, dim3((unsigned)((a.units + 3) / 4)), dim3(256), a);
+  return hipGetLastError();
+}
+
+hipError_t launch_srswa_decode(int dtype, int head_dim, const DecodeArgs& a, hipStream_t s) {
+  UOCR_DISPATCH(k_srswa_decode, dim3((unsigned)a.units), dim3(64 * a.waves), a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_index(int dtype, int head_dim, const IndexArgs& a, hipStream_t s) {
+  const size_t items = (size_t)a.units * a.nb_cap;
+  size_t wgs = (items + kWaves - 1) / kWaves;
+  if (wgs > 8192) wgs = 8192;
+  if (wgs == 0) return hipSuccess;
+  UOCR_DISPATCH(k_block_index, dim3((unsigned)wgs), dim3(64 * kWaves), a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_score(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s) {
+  if (a.nb_cap == 0) return hipSuccess;
+  UOCR_DISPATCH(k_block_score, dim3((unsigned)(a.units * a.parts)), dim3(256), a);
+  return hipGetLastError();
+}
+
+hipError_t launch_entmax_topk(const TopkArgs& a, hipStream_t s) {
+  k_entmax_topk<<<dim3(a.units), dim3(kTopkThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_srswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.d.units);
+  if (a.d.waves == 8) {
+    if (dtype == 0 && head_dim == 64) k_srswa_step<0, 64, 512><<<grid, 512, 0, s>>>(a);
+    else if (dtype == 0 && head_dim == 128) k_srswa_step<0, 128, 512><<<grid, 512, 0, s>>>(a);
+    else if (dtype == 1 && head_dim == 64) k_srswa_step<1, 64, 512><<<grid, 512, 0, s>>>(a);
+    else if (dtype == 1 && head_dim == 128) k_srswa_step<1, 128, 512><<<grid, 512, 0, s>>>(a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (dtype == 0 && head_dim == 64) k_srswa_step<0, 64, 256><<<grid, 256, 0, s>>>(a);
+    else if (dtype == 0 && head_dim == 128) k_srswa_step<0, 128, 256><<<grid, 256, 0, s>>>(a);
+    else if (dtype == 1 && head_dim == 64) k_srswa_step<1, 64, 256><<<grid, 256, 0, s>>>(a);
+    else if (dtype == 1 && head_dim == 128) k_srswa_step<1, 128, 256><<<grid, 256, 0, s>>>(a);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((long)a.d.units * a.d.splits));
+  UOCR_DISPATCH(k_rswa_step, grid, dim3(64 * a.d.waves), a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.d.splits == 1) return e;
+  UOCR_DISPATCH(k_split_merge, dim3((unsigned)((a.d.units + 3) / 4)), dim3(256), a.d);
+  return hipGetLastError();
+}
+
+}  // namespace uocr

@@ -236,18 +236,25 @@ def step_inputs(w: Workload, step: int):
     return step_query(w, step), k, v
 
 
-def initial_ring(w: Workload):
-    """Ring K/V [B][H][n][D] holding tokens max(0, t0-n) .. t0-1 in slot tau mod n
-    (slots never written are NaN) and the generated count t_gen[B] = t0."""
+def initial_ring(w: Workload, t0=None):
+    """Ring K/V [B][H][n][D] holding, for sequence b, tokens max(0, t0_b-n) ..
+    t0_b-1 in slot tau mod n (slots never written are NaN) and the generated
+    count t_gen[B] = t0.  t0 defaults to w.t0 for every sequence."""
     n = w.window
+    t0s = np.full((w.batch,), w.t0, dtype=np.int64) if t0 is None else np.asarray(t0, dtype=np.int64)
     Kr = nan_fill((w.batch, w.heads, n, w.head_dim), w.dtype)
     Vr = nan_fill((w.batch, w.heads, n, w.head_dim), w.dtype)
-    for tau in range(max(0, w.t0 - n), w.t0):
+    lo = int(max(0, (t0s - n).min())) if len(t0s) else 0
+    hi = int(t0s.max()) if len(t0s) else 0
+    for tau in range(lo, hi):
+        seqs = [b for b in range(w.batch) if t0s[b] - n <= tau < t0s[b]]
+        if not seqs:
+            continue
         k, v = history_token(w, tau)
-        Kr[:, :, tau % n, :] = k
-        Vr[:, :, tau % n, :] = v
-    t_gen = np.full((w.batch,), w.t0, dtype=np.int32)
-    return Kr, Vr, t_gen
+        for b in seqs:
+            Kr[b, :, tau % n, :] = k[b]
+            Vr[b, :, tau % n, :] = v[b]
+    return Kr, Vr, t0s.astype(np.int32)
 
 
 def step_pool(w: Workload, steps: int):

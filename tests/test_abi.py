@@ -1,0 +1,128 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, and rejects invalid arguments with the documented status
+before launching anything.  No kernel runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from long_context_decode_attn_amd import uocr as U
+    try:
+        return U, U.load_library()
+    except RuntimeError as e:  # not built in this checkout
+        pytest.skip(str(e))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "uocr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(uocr_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    U, lib = _lib()
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(U.EXPORTED) == names
+
+
+def test_version_and_status_strings():
+    U, lib = _lib()
+    assert U.uocr_version() == 10000
+    for code in range(0, -8, -1):
+        assert U.uocr_status_string(code) not in ("", "unknown status")
+    assert U.uocr_status_string(-99) == "unknown status"
+
+
+def _shape(U, **kw):
+    base = dict(batch=2, heads=3, head_dim=128, prefix_cap=320, window=128, dtype=1, scale=0.088)
+    base.update(kw)
+    return U._Shape(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10004)
+
+
+def _rswa(lib, sh, q=FAKE, ws=None, wsb=0, splits=1, out=FAKE):
+    return lib.uocr_rswa_decode(ctypes.byref(sh), q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, out, ws, wsb, splits, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 7, -3), ("batch", 0, -2), ("heads", -1, -2), ("head_dim", 96, -6), ("prefix_cap", -1, -2),
+    ("prefix_cap", (1 << 20) + 1, -2), ("window", 0, -2), ("window", 1025, -2), ("scale", float("inf"), -2),
+])
+def test_shape_validation(field, value, status):
+    U, lib = _lib()
+    sh = _shape(U, **{field: value})
+    assert _rswa(lib, sh) == status
+    assert U.uocr_last_error()
+
+
+def test_null_alignment_and_workspace_errors():
+    U, lib = _lib()
+    sh = _shape(U)
+    assert lib.uocr_rswa_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 1, None) == -1
+    assert _rswa(lib, sh, q=None) == -1
+    assert _rswa(lib, sh, q=ODD) == -5
+    assert _rswa(lib, sh, out=ODD) == -5
+    # more than one split needs a workspace of the queried size
+    need = lib.uocr_rswa_workspace_bytes(ctypes.byref(sh), 4)
+    assert need > 0
+    assert _rswa(lib, sh, splits=4) == -1
+    assert _rswa(lib, sh, splits=4, ws=FAKE, wsb=need - 1) == -4
+    assert _rswa(lib, sh, splits=-1) == -2
+    assert lib.uocr_rswa_workspace_bytes(ctypes.byref(sh), 1) == 0
+
+
+def test_route_validation():
+    U, lib = _lib()
+    sh = _shape(U)
+    for block, idx, k, status in [(16, 32, 16, -6), (32, 64, 16, -6), (32, 32, 0, -2), (32, 32, 65, -2)]:
+        r = U._Route(block, idx, k)
+        assert lib.uocr_block_score(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+        assert lib.uocr_entmax15_topk(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, FAKE, None, FAKE, None) == status
+    big = _shape(U, prefix_cap=4097 * 32)
+    r = U._Route(32, 32, 16)
+    assert lib.uocr_entmax15_topk(ctypes.byref(big), ctypes.byref(r), FAKE, FAKE, FAKE, None, FAKE, None) == -6
+    assert lib.uocr_srswa_decode(ctypes.byref(sh), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                 FAKE, 1, None) == -1
+    assert lib.uocr_srswa_decode(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                 FAKE, FAKE, 1, None) == -1
+    assert lib.uocr_srswa_decode(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                 FAKE, FAKE, -1, None) == -2
+    assert lib.uocr_ring_append(ctypes.byref(sh), FAKE, FAKE, FAKE, ODD, FAKE, None) == -5
+    assert lib.uocr_block_index_build(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, None, FAKE, None) == -1
+
+
+def test_split_geometry():
+    U, lib = _lib()
+    for B, H, m in [(64, 10, 2592), (512, 10, 288), (1, 2, 528), (32, 10, 10240), (8, 10, 32000), (1, 1, 0)]:
+        sh = U.Shape(B, H, 128, m)
+        S = U.uocr_rswa_splits(sh)
+        assert 1 <= S <= max(1, -(-(m + 128) // 32))
+        assert U.uocr_rswa_splits(sh, 10 ** 6) <= -(-(m + 128) // 16)
+    r = U.Route()
+    sh = U.Shape(8, 10, 128, 32000)
+    assert U.uocr_srswa_splits(sh, r) == 8            # waves per unit
+    assert U.uocr_srswa_splits(sh, r, 1) == 1
+    assert U.uocr_srswa_splits(sh, r, 99) == 8
+
+
+def test_product_path_has_no_oracle_or_fallback():
+    """Nothing in the package imports the oracle, and the binding has no
+    CPU path: every compute function goes through libuocr.so."""
+    pkg = os.path.join(ROOT, "long_context_decode_attn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "uocr_oracle" not in text, f

@@ -1,0 +1,185 @@
+"""GPU parity of the ring append and dense R-SWA decode against the oracle,
+called through the C ABI (libuocr.so)."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_attn_amd import synth as S
+from long_context_decode_attn_amd import uocr as U
+from long_context_decode_attn_amd.session import DecodeSession, to_device, to_host
+from oracle import uocr_oracle as O
+from tests._gpu_common import HostMirror, assert_close, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _ring_bits_equal(dev: torch.Tensor, host64: np.ndarray) -> bool:
+    got = to_host(dev)
+    return bool(np.array_equal(np.isnan(got), np.isnan(host64)) and
+                np.array_equal(np.nan_to_num(got), np.nan_to_num(host64)))
+
+
+def test_ring_append_bit_exact_with_wrapping_pointer():
+    need_gpu()
+    for dtype, D in [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)]:
+        w = S.Workload("ring", batch=3, heads=2, head_dim=D, dtype=dtype, pages=0, prompt=8, t0=0,
+                       steps=70, seed=41)
+        say("ring append", dtype, D)
+        n = 16
+        w = w.replace(window=n)
+        Kr, Vr, _ = S.initial_ring(w)
+        t0 = np.array([0, 5, 1000], dtype=np.int32)     # different start pointers per sequence
+        sess = DecodeSession(w, ring=(Kr, Vr, t0))
+        host = HostMirror(w, ring=(Kr, Vr, t0))
+        for step in range(40):
+            q, k, v = S.step_inputs(w, step)
+            sess.append(to_device(k, dtype), to_device(v, dtype))
+            host.append(k, v)
+            torch.cuda.synchronize()
+            assert np.array_equal(sess.t_gen.cpu().numpy(), host.t_gen.astype(np.int32)), step
+            assert _ring_bits_equal(sess.k_ring, host.Kr), step
+            assert _ring_bits_equal(sess.v_ring, host.Vr), step
+            # cache size after the step is m + min(n, t)
+            for b in range(w.batch):
+                assert O.cache_len(w.prefix_len, n, int(host.t_gen[b])) == \
+                    w.prefix_len + len(O.window_positions(int(host.t_gen[b]), n))
+
+
+def _run_dense(w, steps, check_every=1, units=None, num_splits=0, prefix_cap=None, prefix_len=None, t_gen=None,
+               fused=False):
+    """Run `steps` decode steps on the GPU and on the oracle; compare the
+    chosen units every `check_every` steps (and the ring state bit for bit)."""
+    Kr, Vr, tg = S.initial_ring(w, t_gen)
+    kv = S.prefix_kv(w, prefix_cap)
+    sess = DecodeSession(w, prefix_cap=prefix_cap, num_splits=num_splits, prefix_kv=kv, ring=(Kr, Vr, tg),
+                         fused=fused)
+    host = HostMirror(w, prefix_cap=prefix_cap, prefix_kv=kv, ring=(Kr, Vr, tg))
+    if prefix_len is not None:
+        sess.prefix_len.copy_(torch.tensor(prefix_len, dtype=torch.int32))
+        host.prefix_len = np.asarray(prefix_len)
+    units = [(b, h) for b in range(w.batch) for h in range(w.heads)] if units is None else units
+    worst = (0.0, 0.0)
+    for step in range(steps):
+        q, k, v = S.step_inputs(w, step)
+        out = sess.step(to_device(q, w.dtype), to_device(k, w.dtype), to_device(v, w.dtype))
+        host.append(k, v)
+        if step % check_every and step != steps - 1:
+            continue
+        assert np.array_equal(sess.t_gen.cpu().numpy(), host.t_gen.astype(np.int32))
+        if w.units <= 64:
+            assert _ring_bits_equal(sess.k_ring, host.Kr) and _ring_bits_equal(sess.v_ring, host.Vr)
+        got = to_host(out)
+        assert np.isfinite(got).all()
+        qd = S.widen(q, w.dtype)
+        ref = np.stack([O.rswa_unit(qd[b, h], host.Kp[b, h], host.Vp[b, h], int(host.prefix_len[b]),
+                                    *host.window(b, h), w.scale) for b, h in units])
+        sel = np.stack([got[b, h] for b, h in units])
+        e = assert_close(sel, ref, w.dtype, f"{w.name} step {step}")
+        worst = max(worst, e)
+    return worst
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_dense_fp32_two_pages_every_step_three_wraps(fused):
+    """2 pages + 16 prompt, fp32, D = 64, ring from empty, 512 steps (fill +
+    3 wraps), every step checked."""
+    need_gpu()
+    w = S.WORKLOADS["dense-2p-b1-fp32"]
+    say("dense fp32", w, "fused" if fused else "")
+    worst = _run_dense(w, w.steps, fused=fused)
+    say("worst", worst)
+
+
+@pytest.mark.parametrize("num_splits,fused", [(0, False), (1, False), (3, False), (7, False), (0, True),
+                                              (1, True), (5, True)])
+def test_dense_bf16_ragged_prefix_and_window(num_splits, fused):
+    """Several tiles and ragged tails: per-sequence prefix lengths (full,
+    partial, zero) and generated counts (empty ring, partial, wrapped), NaN in
+    every unused prefix row and ring slot."""
+    need_gpu()
+    w = S.Workload("ragged", batch=4, heads=3, head_dim=128, dtype="bf16", pages=1, prompt=44, t0=0,
+                   steps=6, seed=77)
+    say("ragged dense, splits", num_splits, "fused" if fused else "")
+    _run_dense(w, 6, prefix_cap=320, prefix_len=[300, 37, 0, 1], t_gen=[0, 5, 200, 0],
+               num_splits=num_splits, fused=fused)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_dense_other_dtypes_and_dims(dtype, D):
+    need_gpu()
+    w = S.Workload("dims", batch=2, heads=3, head_dim=D, dtype=dtype, pages=1, prompt=3, t0=130,
+                   steps=4, seed=78)
+    say("dense", dtype, D)
+    _run_dense(w, 4, prefix_len=[259, 100])
+
+
+def test_dense_empty_key_set_gives_zero():
+    need_gpu()
+    w = S.Workload("empty", batch=2, heads=2, head_dim=128, dtype="bf16", pages=0, prompt=0, t0=0,
+                   steps=1, seed=5)
+    sess = DecodeSession(w, prefix_cap=0)
+    q, _, _ = S.step_inputs(w, 0)
+    sess.attend(to_device(q, "bf16"))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(sess.out), np.zeros((2, 2, 128)))
+
+
+@pytest.mark.parametrize("name,fused", [("dense-10p-b64", False), ("dense-1p-b512", False),
+                                        ("dense-10p-b64", True), ("dense-1p-b512", True)])
+def test_dense_full_size_sampled(name, fused):
+    """Full-size dense workloads in the benchmark's launch configuration:
+    every output finite, 32 sampled units per step checked."""
+    need_gpu()
+    w = S.WORKLOADS[name]
+    say("full-size dense", name, "fused" if fused else "")
+    rng = np.random.default_rng(3)
+    units = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(32)]
+    _run_dense(w, 3, units=units, fused=fused)
+
+
+def test_fused_step_leaves_input_counts_and_matches_separate_calls():
+    """The fused dense step == append + decode: same ring, same counts (in the
+    other buffer), bitwise-identical output; t_gen_in is not modified."""
+    need_gpu()
+    w = S.WORKLOADS["dense-10p-b64"].replace(batch=3)
+    kv = S.prefix_kv(w)
+    ring = S.initial_ring(w, [6144, 5, 127])
+    a = DecodeSession(w, prefix_kv=kv, ring=ring)
+    f = DecodeSession(w, prefix_kv=kv, ring=ring, fused=True)
+    for step in range(4):
+        q, k, v = (to_device(x, w.dtype) for x in S.step_inputs(w, step))
+        before = f.t_gen.clone()
+        oa = a.step(q, k, v).clone()
+        of = f.step(q, k, v).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(f.t_gen_next, before)          # the input buffer is untouched
+        assert torch.equal(f.t_gen, a.t_gen)
+        assert torch.equal(f.k_ring.view(torch.int16), a.k_ring.view(torch.int16))
+        assert torch.equal(f.v_ring.view(torch.int16), a.v_ring.view(torch.int16))
+        assert torch.equal(oa.view(torch.int16), of.view(torch.int16))
+
+
+def test_dense_deterministic_and_resumable():
+    """Two runs give bitwise identical outputs; the state (ring K/V + t_gen)
+    copied out mid-run and restored into fresh buffers continues identically."""
+    need_gpu()
+    w = S.WORKLOADS["dense-10p-b64"].replace(batch=4)
+    kv = S.prefix_kv(w)
+    ring = S.initial_ring(w)
+    a = DecodeSession(w, prefix_kv=kv, ring=ring)
+    b = DecodeSession(w, prefix_kv=kv, ring=ring)
+    outs_a, outs_b = [], []
+    runner = b
+    for step in range(6):
+        q, k, v = (to_device(x, w.dtype) for x in S.step_inputs(w, step))
+        outs_a.append(a.step(q, k, v).clone())
+        outs_b.append(runner.step(q, k, v).clone())
+        if step == 2:   # checkpoint b after this step, restore into a fresh session
+            c = DecodeSession(w, prefix_kv=kv, ring=ring)
+            c.k_ring.copy_(b.k_ring)
+            c.v_ring.copy_(b.v_ring)
+            c.t_gen.copy_(b.t_gen)
+            runner = c
+    torch.cuda.synchronize()
+    for x, y in zip(outs_a, outs_b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
