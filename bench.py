@@ -31,6 +31,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
+
+# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of
+# this script (summaries under profiles/), scaled by what the counters read for
+# a plain device copy of known size: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  Valid
+# only for the kernel source they were taken on (sha256 prefix of
+# uocr_kernels.hip); otherwise the traffic is reported as null.
+COUNTER_TRAFFIC = {
+    # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
+}
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
 
@@ -47,6 +56,9 @@ def parse():
                     help="fused: one uocr_*_step launch per step; separate: one launch per row")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy (known bytes) so that a "
+                         "counter profile of this run can scale FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -69,6 +81,19 @@ def algorithmic_bytes(w, live_blocks_per_unit=None):
     else:
         b["uocr_rswa_decode"] = units * (row + 2 * (w.prefix_len + wnd) * row + row) + w.batch * 8
     return b
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "long_context_decode_attn_amd", "csrc", "uocr_kernels.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    rec = COUNTER_TRAFFIC.get((kernel, workload))
+    if rec is None or rec[0] != kernel_source_hash():
+        return None
+    return rec[1] + rec[2]
 
 
 def index_bytes(w):
@@ -164,6 +189,15 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         idx_ms = e0.elapsed_time(e1) / len(layers)
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     pool_n = 64
     qp, kp, vp = S.step_pool(w, pool_n)
@@ -285,12 +319,14 @@ def main():
                    "mode": args.mode, "accumulate": "f32 attention, f64 routing",
                    "parallelism": "single-gpu"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic(dom, w.name)},
         "step_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "timing": (f"HIP graph of {G} steps replayed {reps} times" + (f" + {rest} steps" if rest else "")
                    + f"; eager launches: {eager_ms_per_step * 1e3:.2f} us/step"),
         "eager_ms_per_step": round(eager_ms_per_step, 5),
         "kernels": kernels,
+        "kernel_source": kernel_source_hash(),
     }
     if w.sparse:
         result["routing"] = {"live_blocks_per_unit": round(live / w.units, 3),

@@ -120,9 +120,9 @@ void rswa_geometry(const uocr_shape* sh, int32_t req, int* splits, int* chunk) {
   if (req > 0) {
     S = req;
   } else {
-    // aim at ~4096 workgroups over the chip (256 CUs), >= 256 keys each
-    const int want = (4096 + units - 1) / units;
-    const int cap = (L + 255) / 256;
+    // aim at ~2048 workgroups over the chip (256 CUs), >= 512 keys each
+    const int want = (2048 + units - 1) / units;
+    const int cap = (L + 511) / 512;
     S = want < cap ? want : cap;
   }
   if (S > max_useful) S = max_useful;
