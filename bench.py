@@ -39,6 +39,10 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
+    ("uocr_srswa_step", "srswa-40p-b32"): ("87d6d8af75a9148e", 45059883, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("87d6d8af75a9148e", 18760819, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("87d6d8af75a9148e", 892436856, 1720756),
+    ("uocr_rswa_step", "dense-1p-b512"): ("87d6d8af75a9148e", 1092080498, 3940462),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
