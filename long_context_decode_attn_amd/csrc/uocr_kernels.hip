@@ -754,13 +754,20 @@ __device__ __forceinline__ T block_max(T x, T* sh) {
   return r;
 }
 
+struct NoOverlap {
+  __device__ void operator()() const {}
+};
+
 // Routing of one unit from its nb scores `s` (global or LDS).  Writes topk
 // entries of o_idx / o_prob (may be null) / o_bias and, when l_idx is not
 // null, the same indices and biases to l_idx / l_bias.  Every thread of the
-// workgroup must call it.
-template <int NT>
+// workgroup must call it.  `others` runs exactly once on every wave but wave
+// 0, while wave 0 works alone on the usual (one-wave) path: it lets a caller
+// overlap independent work with the routing.
+template <int NT, typename F = NoOverlap>
 __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int topk, int32_t* o_idx, float* o_prob,
-                                  float* o_bias, int* l_idx, float* l_bias, TopkSmem<NT>& sm) {
+                                  float* o_bias, int* l_idx, float* l_bias, TopkSmem<NT>& sm,
+                                  const F& others = F()) {
   constexpr int PT = kMaxBlocks / NT;  // values per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kk = min(topk, nb);
@@ -773,7 +780,10 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
       l_bias[i] = -INFINITY;
     }
   }
-  if (kk == 0) return;
+  if (kk == 0) {
+    if (wave != 0) others();
+    return;
+  }
 
   // ---- one-wave path (nb <= 1024 and a candidate set of <= 64 blocks) ----
   // Wave 0 alone: no workgroup barrier until the end.  Lane l owns blocks
@@ -784,7 +794,9 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
   // broadcast loop over A gives each lane its rank, and one over the entmax
   // candidates (exact d < 2, compacted first) the prefix statistics of the
   // sorted order at the end of each candidate's tie group.
+  if (nb > 64 * kWaveBlocks && wave != 0) others();
   if (nb <= 64 * kWaveBlocks) {
+    if (wave != 0) others();
     if (wave == 0) {
       float sv[kWaveBlocks];
       float lmax = -INFINITY;
@@ -1240,13 +1252,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
 // STREAM selects nontemporal loads (better when the grid fills the chip and
 // the step is bandwidth-bound) or plain loads (lower latency, better for a
 // few units per CU).
-// The window does not depend on the routing, so it is attended first, while
-// the block keys are in flight:
 //   1. write the new token into its ring slot; issue the loads of the block
-//      keys; q_idx = P^T q (fp64); attend over the window (the new token's
-//      row is taken from k_new / v_new, so no wave waits for the ring write);
-//   2. block scores into LDS; entmax + top-k in LDS;
-//   3. attend over the live selected blocks; merge the waves through LDS.
+//      keys; q_idx = P^T q (fp64);
+//   2. block scores into LDS;
+//   3. entmax + top-k on wave 0 while waves 1 .. W-1 attend over the window,
+//      which does not depend on the routing (the new token's row is taken
+//      from k_new / v_new, so no wave waits for the ring write);
+//   4. attend over the live selected blocks; merge the waves through LDS.
 template <int DT, int D, int NT, bool STREAM>
 __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a) {
   using G = Geo<DT, D>;
@@ -1317,26 +1329,10 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a
     s_red[sl][i] = acc;
   }
 
-  // window: wave w takes rows [w*WR, w*WR + WR) of the visible window
   float q[G::E];
   load_q<DT, D>(d.q, unit, c, d.qscale, q);
   State<G::E> st;
   st.init();
-  {
-    // every slot of the ring is addressable: read this wave's share of all n
-    // slots and let only the first w count
-    const int WR = (n + W - 1) / W;
-    const int r0 = wave * WR, r1 = min(r0 + WR, n);
-    if (r0 < r1) {
-      const size_t base = ((size_t)unit * n + r0) * G::ROWB + cb;
-      const size_t nbase = (size_t)unit * G::ROWB + cb;
-      // a 128-row window over 8 waves is 16 rows per wave: half the loads in flight
-      constexpr int UW = (G::U / 2) > 0 ? G::U / 2 : 1;
-      attend_range<DT, D, UW, STREAM>(static_cast<const char*>(d.k_ring) + base, static_cast<const char*>(d.v_ring) + base,
-                              r1 - r0, 0.f, q, st, grp, slot - r0, static_cast<const char*>(a.k_new) + nbase,
-                              static_cast<const char*>(a.v_new) + nbase, w - r0);
-    }
-  }
   __syncthreads();
   if (tid < kIdxDim) {
     double sum = 0.0;
@@ -1372,9 +1368,26 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a
   }
   __syncthreads();
 
+  // Window attention on waves 1 .. W-1 while wave 0 routes: every slot of
+  // the ring is addressable, so each of these waves reads its share of all n
+  // slots and lets only the first w count; the new token's row is taken from
+  // k_new / v_new.
+  auto window = [&]() {
+    const int WR = (n + W - 2) / (W - 1);
+    const int r0 = (wave - 1) * WR, r1 = min(r0 + WR, n);
+    if (r0 < r1) {
+      const size_t base = ((size_t)unit * n + r0) * G::ROWB + cb;
+      const size_t nbase = (size_t)unit * G::ROWB + cb;
+      constexpr int UW = (20 + G::RPL - 1) / G::RPL < 8 ? (20 + G::RPL - 1) / G::RPL : 8;
+      attend_range<DT, D, UW, STREAM>(static_cast<const char*>(d.k_ring) + base,
+                                      static_cast<const char*>(d.v_ring) + base, r1 - r0, 0.f, q, st, grp,
+                                      slot - r0, static_cast<const char*>(a.k_new) + nbase,
+                                      static_cast<const char*>(a.v_new) + nbase, w - r0);
+    }
+  };
   const size_t so = (size_t)unit * d.topk;
   entmax_topk_block<NT>(s_scores, nb, d.topk, a.sel_idx + so, a.sel_prob ? a.sel_prob + so : nullptr,
-                        a.sel_bias + so, l_idx, l_bias, tsm);
+                        a.sel_bias + so, l_idx, l_bias, tsm, window);
   __syncthreads();
 
   // live selected blocks, dealt round-robin to the waves
