@@ -119,6 +119,18 @@ __device__ __forceinline__ double dpp(double x) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
+// Value of the lane 16 (32) positions away, through the gfx950 row / half
+// swaps: with both operands equal, permlane16_swap returns rows (0, 0, 2, 2)
+// and (1, 1, 3, 3), permlane32_swap the halves (lo, lo) and (hi, hi).
+__device__ __forceinline__ float xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // Sum over groups of N lanes (N = 2 .. 32, aligned); every lane of a group
 // gets the group's sum.
 template <int N, typename T>
@@ -127,7 +139,10 @@ __device__ __forceinline__ T group_sum(T x) {
   if constexpr (N > 2) x += dpp<kDppXor2>(x);
   if constexpr (N > 4) x += dpp<kDppHalfMirror>(x);
   if constexpr (N > 8) x += dpp<kDppMirror>(x);
-  if constexpr (N > 16) x += __shfl_xor(x, 16);
+  if constexpr (N > 16) {
+    if constexpr (sizeof(T) == 4) x += xor16(x);
+    else x += __shfl_xor(x, 16);
+  }
   return x;
 }
 
@@ -280,21 +295,28 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ K, const c
 
 // Merge the RPL row groups of a wave: afterwards every lane holds the wave's
 // state for its chunk.
-template <int LPR, int E>
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float x) {
+  if constexpr (OFF == 16) return xor16(x);
+  else if constexpr (OFF == 32) return xor32(x);
+  else return __shfl_xor(x, OFF);
+}
+
+template <int LPR, int E, int OFF = LPR>
 __device__ __forceinline__ void merge_groups(State<E>& st) {
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-    const float mo = __shfl_xor(st.m, off);
-    const float lo = __shfl_xor(st.l, off);
+  if constexpr (OFF < 64) {
+    const float mo = lane_xor<OFF>(st.m);
+    const float lo = lane_xor<OFF>(st.l);
     const float mn = fmaxf(st.m, mo);
     const float a = fexp2(st.m - mn), b = fexp2(mo - mn);
     st.l = st.l * a + lo * b;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const float ao = __shfl_xor(st.acc[e], off);
+      const float ao = lane_xor<OFF>(st.acc[e]);
       st.acc[e] = st.acc[e] * a + ao * b;
     }
     st.m = mn;
+    merge_groups<LPR, E, OFF * 2>(st);
   }
 }
 
@@ -787,22 +809,27 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
 
   // ---- one-wave path (nb <= 1024 and a candidate set of <= 64 blocks) ----
   // Wave 0 alone: no workgroup barrier until the end.  Lane l owns blocks
-  // [16 l, 16 l + 16).  With d = smax - s in fp32 (monotone in s), the set
-  // A = {d < T}, T = 4, 8, 16, ... until it holds kk blocks, contains the top
-  // kk (ties of the kk-th included) and the entmax support (exact d < 2 gives
-  // fp32 d <= 2 < 4).  A is compacted in index order, one block per lane; a
-  // broadcast loop over A gives each lane its rank, and one over the entmax
-  // candidates (exact d < 2, compacted first) the prefix statistics of the
-  // sorted order at the end of each candidate's tie group.
+  // l, l + 64, l + 128, ... (slot e holds block l + 64 e), so index order is
+  // (slot, lane) order and an ordered compaction needs only ballots.  With
+  // d = smax - s in fp32 (monotone in s), the set A = {d < T}, T = 4, 8, 16,
+  // ... until it holds kk blocks, contains the top kk (ties of the kk-th
+  // included) and the entmax support (exact d < 2 gives fp32 d <= 2 < 4).  A
+  // is compacted in index order into LDS; each lane takes one block of A and
+  // counts, over broadcast LDS reads of A, the blocks ranked before it and
+  // (for an entmax candidate) the prefix statistics of the sorted order at the
+  // end of its tie group.
   if (nb > 64 * kWaveBlocks && wave != 0) others();
   if (nb <= 64 * kWaveBlocks) {
     if (wave != 0) others();
     if (wave == 0) {
+      // the routing is the critical path of the step: let this wave win the
+      // issue arbitration against the waves attending over the window
+      __builtin_amdgcn_s_setprio(3);
       float sv[kWaveBlocks];
       float lmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < kWaveBlocks; ++e) {
-        const int j = lane * kWaveBlocks + e;
+        const int j = e * 64 + lane;
         sv[e] = j < nb ? s[j] : -INFINITY;
         lmax = fmaxf(lmax, sv[e]);
       }
@@ -822,27 +849,32 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
         T = T * 2.f;  // reaches +inf, where every finite d counts
       }
       if (nA <= 64) {
-        int c = 0, cc = 0;
+        // ordered compaction of A (and of the entmax candidates) by ballots
+        int base = 0, cbase = 0;
 #pragma unroll
         for (int e = 0; e < kWaveBlocks; ++e) {
-          c += dv[e] < T ? 1 : 0;
-          cc += ((double)sv[e] - dmax) * 0.5 > -1.0 ? 1 : 0;
-        }
-        int pos = wave_prefix_small(c);
-        int cpos = wave_prefix_small(cc);
-        const int nC = wave_sum(cc);
-#pragma unroll
-        for (int e = 0; e < kWaveBlocks; ++e) {
-          if (dv[e] < T) {
-            sm.a.val[pos] = sv[e];
-            sm.a.idx[pos] = lane * kWaveBlocks + e;
-            ++pos;
+          const bool in = dv[e] < T;
+          const bool cd = ((double)sv[e] - dmax) * 0.5 > -1.0;
+          const uint64_t m = __ballot(in);
+          const uint64_t mc = __ballot(cd);
+          const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          const int cbelow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
+          if (in) {
+            sm.a.val[base + below] = sv[e];
+            sm.a.idx[base + below] = e * 64 + lane;
           }
-          if (((double)sv[e] - dmax) * 0.5 > -1.0) {
-            sm.a.rank[cpos] = __float_as_int(sv[e]);  // candidate scores
-            ++cpos;
-          }
+          if (cd) sm.a.rank[cbase + cbelow] = __float_as_int(sv[e]);  // candidate scores
+          base += __popcll(m);
+          cbase += __popcll(mc);
         }
+        const int nC = cbase;
+        const int nA4 = (nA + 3) & ~3, nC4 = (nC + 3) & ~3;
+        if (lane < nA4 - nA) {
+          sm.a.val[nA + lane] = -INFINITY;  // ranks below every block, never >= a real score
+          sm.a.idx[nA + lane] = 0x7fffffff;
+        }
+        if (lane < nC4 - nC) sm.a.rank[nC + lane] = __float_as_int(-INFINITY);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -851,22 +883,30 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
         const int ii = mine ? sm.a.idx[lane] : 0x7fffffff;
         const double vi = ((double)si - dmax) * 0.5;
         const bool cand = mine && vi > -1.0;
+        const float4* val4 = reinterpret_cast<const float4*>(sm.a.val);
+        const int4* idx4 = reinterpret_cast<const int4*>(sm.a.idx);
         int rank = 0;
-        for (int k = 0; k < nA; ++k) {
-          const float sk = readlane_f(si, k);
-          const int ik = __builtin_amdgcn_readlane(ii, k);
-          rank += (sk > si || (sk == si && ik < ii)) ? 1 : 0;
+#pragma unroll 4
+        for (int k4 = 0; k4 < nA4 / 4; ++k4) {
+          const float4 sk = val4[k4];
+          const int4 ik = idx4[k4];
+          rank += (sk.x > si || (sk.x == si && ik.x < ii)) + (sk.y > si || (sk.y == si && ik.y < ii)) +
+                  (sk.z > si || (sk.z == si && ik.z < ii)) + (sk.w > si || (sk.w == si && ik.w < ii));
         }
-        const float ci = lane < nC ? __int_as_float(sm.a.rank[lane]) : -INFINITY;
+        const float4* cv4 = reinterpret_cast<const float4*>(sm.a.rank);
         int r = 0;
         double s1 = 0.0, s2 = 0.0;
-        for (int k = 0; k < nC; ++k) {
-          const float sk = readlane_f(ci, k);
-          if (sk >= si) {
-            const double vk = ((double)sk - dmax) * 0.5;
-            ++r;
-            s1 += vk;
-            s2 += vk * vk;
+        for (int k4 = 0; k4 < nC4 / 4; ++k4) {
+          const float4 c4 = cv4[k4];
+          const float ck[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (ck[k] >= si) {
+              const double vk = ((double)ck[k] - dmax) * 0.5;
+              ++r;
+              s1 += vk;
+              s2 += vk * vk;
+            }
           }
         }
         int rr = 0;
@@ -886,10 +926,10 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
           const int at = __builtin_amdgcn_mbcnt_hi((uint32_t)(sm_ >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)sm_, 0u));
           const double dd = vi - tau;
-          const double p = dd > 0.0 ? dd * dd : 0.0;
-          const float bias = p > 0.0 ? (float)log(p) : -INFINITY;
+          const float p = dd > 0.0 ? (float)(dd * dd) : 0.f;
+          const float bias = p > 0.f ? logf(p) : -INFINITY;
           o_idx[at] = ii;
-          if (o_prob) o_prob[at] = (float)p;
+          if (o_prob) o_prob[at] = p;
           o_bias[at] = bias;
           if (l_idx) {
             l_idx[at] = ii;
@@ -898,6 +938,7 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
         }
       }
       if (lane == 0) sm.digit = nA <= 64 ? 1u : 0u;
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
     const bool done = sm.digit == 1u;
