@@ -130,6 +130,35 @@ __device__ __forceinline__ float xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
+// x plus the value of the lane 16 (32) positions away.  A swap with both
+// operands equal hands each lane its own and its partner's value in a fixed
+// order (lower row first), so both lanes of a pair add the same two numbers
+// in the same order and get bit-identical sums, with no lane select.
+__device__ __forceinline__ float sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ double join(unsigned lo, unsigned hi) {
+  return __longlong_as_double(((long long)hi << 32) | lo);
+}
+__device__ __forceinline__ double sum16(double x) {
+  const long long u = __double_as_longlong(x);
+  const unsigned lo = (unsigned)(u & 0xffffffffll), hi = (unsigned)(u >> 32);
+  const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  return join(l[0], h[0]) + join(l[1], h[1]);
+}
+__device__ __forceinline__ double sum32(double x) {
+  const long long u = __double_as_longlong(x);
+  const unsigned lo = (unsigned)(u & 0xffffffffll), hi = (unsigned)(u >> 32);
+  const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return join(l[0], h[0]) + join(l[1], h[1]);
+}
 
 // Sum over groups of N lanes (N = 2 .. 32, aligned); every lane of a group
 // gets the group's sum.
@@ -139,10 +168,7 @@ __device__ __forceinline__ T group_sum(T x) {
   if constexpr (N > 2) x += dpp<kDppXor2>(x);
   if constexpr (N > 4) x += dpp<kDppHalfMirror>(x);
   if constexpr (N > 8) x += dpp<kDppMirror>(x);
-  if constexpr (N > 16) {
-    if constexpr (sizeof(T) == 4) x += xor16(x);
-    else x += __shfl_xor(x, 16);
-  }
+  if constexpr (N > 16) x = sum16(x);
   return x;
 }
 
@@ -591,54 +617,157 @@ __global__ __launch_bounds__(512) void k_srswa_decode(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// uocr_block_index_build: one wave per (unit, block); fp64 accumulation
+// Reduce-scatter over aligned groups of N lanes (N = 8, 16 or 32), each lane
+// holding N/2 doubles v[0 .. N/2): afterwards v[0] of every lane is the group
+// total of element rs_elem<N>(lane), and the two lanes of an even/odd pair
+// hold the same element.  Each halving step pairs a lane with one whose step
+// bit differs, keeps the half its bit names and adds the partner's copy of it:
+// the row swap (N = 32) needs no select, the DPP mirrors and the quad xor do.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ int rs_elem(int lane) {
+  int e = 0;
+  if constexpr (N == 32) e = ((lane >> 4) & 1) * 8;
+  if constexpr (N >= 16) e += ((lane & 15) >= 8) * 4;
+  e += ((lane & 7) >= 4) * 2;
+  e += (lane & 3) >= 2;
+  return e;
+}
+
+template <int CTRL, int H>
+__device__ __forceinline__ void rs_dpp_step(double (&v)[H * 2], bool bit) {
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const double keep = bit ? v[k + H] : v[k], send = bit ? v[k] : v[k + H];
+    v[k] = keep + dpp<CTRL>(send);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void reduce_scatter(double (&v)[N / 2], int lane) {
+  constexpr int K = N / 2;
+  if constexpr (N == 32) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const long long ua = __double_as_longlong(v[k]), ub = __double_as_longlong(v[k + 8]);
+      const auto l = __builtin_amdgcn_permlane16_swap((unsigned)(ua & 0xffffffffll), (unsigned)(ub & 0xffffffffll),
+                                                      false, false);
+      const auto h = __builtin_amdgcn_permlane16_swap((unsigned)(ua >> 32), (unsigned)(ub >> 32), false, false);
+      v[k] = join(l[0], h[0]) + join(l[1], h[1]);
+    }
+  }
+  if constexpr (N >= 16) rs_dpp_step<kDppMirror, 4>(*reinterpret_cast<double(*)[8]>(&v[0]), (lane & 15) >= 8);
+  rs_dpp_step<kDppHalfMirror, 2>(*reinterpret_cast<double(*)[4]>(&v[0]), (lane & 7) >= 4);
+  rs_dpp_step<kDppXor2, 1>(*reinterpret_cast<double(*)[2]>(&v[0]), (lane & 3) >= 2);
+  v[0] += dpp<kDppXor1>(v[0]);
+  (void)K;
+}
+
+// ---------------------------------------------------------------------------
+// uocr_block_index_build: each wave owns a contiguous run of (unit, block)
+// items and streams it, loading the next block's rows while it reduces the
+// current one; fp64 accumulation.  Per block: the row sums of every lane's
+// dimensions (exchanged between the row groups of the wave), then the
+// projection with P held transposed in LDS (Pt[i][d], rows padded by 4 floats
+// so the 16-byte reads and the transposing stores spread over the banks):
+// row group g owns outputs g, g + RPL, ... and its lanes split the
+// dimensions, reduced with one reduce-scatter.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_block_index(IndexArgs a) {
   using G = Geo<DT, D>;
   constexpr int E = G::E;
-  __shared__ float Ps[D * kIdxDim];
-  for (int i = threadIdx.x; i < D * kIdxDim; i += blockDim.x) Ps[i] = a.proj[i];
+  constexpr int PD = D + 4;                      // padded row of Pt
+  constexpr int NR = kBlock / G::RPL;            // row loads per lane for a full block
+  constexpr int K = kIdxDim / G::RPL;            // outputs per row group (= LPR / 2)
+  static_assert(K * 2 == G::LPR, "one reduce-scatter element per lane pair");
+  __shared__ __attribute__((aligned(16))) float Pt[kIdxDim * PD];
+  for (int t = threadIdx.x; t < D * kIdxDim; t += blockDim.x) {  // coalesced read of P[d][i]
+    const int d = t / kIdxDim, i = t - d * kIdxDim;
+    Pt[i * PD + d] = a.proj[t];
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int grp = lane / G::LPR, c = lane % G::LPR;
-  const size_t total = (size_t)a.units * a.nb_cap;
-  for (size_t item = (size_t)blockIdx.x * kWaves + (threadIdx.x >> 6); item < total;
-       item += (size_t)gridDim.x * kWaves) {
-    const int unit = (int)(item / a.nb_cap), j = (int)(item - (size_t)unit * a.nb_cap);
-    const int b = unit / a.heads;
-    const int m = min(max(a.prefix_len[b], 0), a.prefix_cap);
+  const long long total = (long long)a.units * a.nb_cap;
+  const long long nw = (long long)gridDim.x * kWaves;
+  const long long per = (total + nw - 1) / nw;
+  const long long beg = ((long long)blockIdx.x * kWaves + (threadIdx.x >> 6)) * per;
+  const long long end = min(total, beg + per);
+  if (beg >= end) return;  // no barrier follows
+
+  auto limit = [&](int unit) { return min(max(a.prefix_len[unit / a.heads], 0), a.prefix_cap); };
+  auto load = [&](uint4 (&kv)[NR], int unit, int j, int nr) {
+    const char* K0 = static_cast<const char*>(a.k_prefix) +
+                     ((size_t)unit * a.prefix_cap + (size_t)j * kBlock) * G::ROWB + c * 16;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int r = grp + u * G::RPL;
+      kv[u] = r < nr ? ld16_stream(K0 + (size_t)r * G::ROWB) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  int unit = (int)(beg / a.nb_cap), j = (int)(beg - (long long)unit * a.nb_cap);
+  int m = limit(unit);
+  int nr = min(kBlock, m - j * kBlock);  // rows of the block inside the prefix (<= 0: none)
+  uint4 kv[NR];
+  load(kv, unit, j, nr);
+  for (long long item = beg; item < end; ++item) {
+    int nunit = unit, nj = j + 1, nm = m;
+    if (nj == a.nb_cap) {
+      ++nunit;
+      nj = 0;
+      nm = item + 1 < end ? limit(nunit) : 0;
+    }
+    const int nnr = item + 1 < end ? min(kBlock, nm - nj * kBlock) : 0;
+    uint4 kn[NR];
+    load(kn, nunit, nj, nnr);
+
     float* dst = a.kbar + item * kIdxDim;
-    if (j * kBlock >= m) {
+    if (nr <= 0) {
       if (lane < kIdxDim) dst[lane] = 0.f;
-      continue;
+    } else {
+      double sum[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) sum[e] = 0.0;
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        float x[E];
+        unpack(kv[u], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) sum[e] += (double)x[e];
+      }
+      // totals over the row groups: every lane ends with the block sums of
+      // dimensions c*E .. c*E+E-1
+      const double inv = 1.0 / (double)nr;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if constexpr (G::LPR < 16) sum[e] += __shfl_xor(sum[e], 8);
+        if constexpr (G::LPR < 32) sum[e] = sum16(sum[e]);
+        sum[e] = sum32(sum[e]) * inv;
+      }
+      double acc[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float4* pr = reinterpret_cast<const float4*>(Pt + (grp + k * G::RPL) * PD + c * E);
+        double t = 0.0;
+#pragma unroll
+        for (int e4 = 0; e4 < E / 4; ++e4) {
+          const float4 p4 = pr[e4];
+          t += (double)p4.x * sum[4 * e4] + (double)p4.y * sum[4 * e4 + 1] + (double)p4.z * sum[4 * e4 + 2] +
+               (double)p4.w * sum[4 * e4 + 3];
+        }
+        acc[k] = t;
+      }
+      reduce_scatter<G::LPR>(acc, lane);
+      if ((lane & 1) == 0) dst[grp + G::RPL * rs_elem<G::LPR>(lane)] = (float)acc[0];
     }
-    const int r0 = j * kBlock, nr = min(kBlock, m - r0);
-    const char* K = static_cast<const char*>(a.k_prefix) + ((size_t)unit * a.prefix_cap + r0) * G::ROWB + c * 16;
-    double sum[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) sum[e] = 0.0;
-#pragma unroll 4
-    for (int r = grp; r < nr; r += G::RPL) {
-      float x[E];
-      unpack(ld16_stream(K + (size_t)r * G::ROWB), x);
-#pragma unroll
-      for (int e = 0; e < E; ++e) sum[e] += (double)x[e];
-    }
-#pragma unroll
-    for (int off = G::LPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < E; ++e) sum[e] += __shfl_xor(sum[e], off);
-    // every lane now holds the block sums of dims c*E .. c*E+E-1; row group
-    // grp produces outputs grp, grp + RPL, ...
-    const double inv = 1.0 / (double)nr;
-    for (int i = grp; i < kIdxDim; i += G::RPL) {
-      double acc = 0.0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc += (double)Ps[(c * E + e) * kIdxDim + i] * (sum[e] * inv);
-      acc = group_sum<G::LPR>(acc);
-      if (c == 0) dst[i] = (float)acc;
-    }
+    for (int u = 0; u < NR; ++u) kv[u] = kn[u];
+    unit = nunit;
+    j = nj;
+    m = nm;
+    nr = nnr;
   }
 }
 
@@ -1539,13 +1668,34 @@ hipError_t launch_srswa_decode(int dtype, int head_dim, const DecodeArgs& a, hip
   return hipGetLastError();
 }
 
+// The index kernel streams: one resident workgroup per slot the kernel's
+// register and LDS use leave on a CU, each wave walking its own run of blocks.
+template <int DT, int D>
+hipError_t launch_block_index_t(const IndexArgs& a, size_t items, hipStream_t s) {
+  static const int cap = [] {
+    int dev = 0, cus = 256, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_block_index<DT, D>, 64 * kWaves, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 2;
+    return cus * per_cu;
+  }();
+  size_t wgs = (items + kWaves - 1) / kWaves;
+  if (wgs > (size_t)cap) wgs = (size_t)cap;
+  k_block_index<DT, D><<<dim3((unsigned)wgs), dim3(64 * kWaves), 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_index(int dtype, int head_dim, const IndexArgs& a, hipStream_t s) {
   const size_t items = (size_t)a.units * a.nb_cap;
-  size_t wgs = (items + kWaves - 1) / kWaves;
-  if (wgs > 8192) wgs = 8192;
-  if (wgs == 0) return hipSuccess;
-  UOCR_DISPATCH(k_block_index, dim3((unsigned)wgs), dim3(64 * kWaves), a);
-  return hipGetLastError();
+  if (items == 0) return hipSuccess;
+  if (dtype == 0 && head_dim == 64) return launch_block_index_t<0, 64>(a, items, s);
+  if (dtype == 0 && head_dim == 128) return launch_block_index_t<0, 128>(a, items, s);
+  if (dtype == 1 && head_dim == 64) return launch_block_index_t<1, 64>(a, items, s);
+  if (dtype == 1 && head_dim == 128) return launch_block_index_t<1, 128>(a, items, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_block_score(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s) {

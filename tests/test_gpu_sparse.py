@@ -52,11 +52,13 @@ def _check_selection(got_idx, got_prob, got_bias, s32, k, s64=None, eps=None, wh
 # ----------------------------------------------------------------------------
 # routing pieces
 # ----------------------------------------------------------------------------
-def test_block_index_and_scores_match_oracle():
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_block_index_and_scores_match_oracle(dtype, head_dim):
     need_gpu()
-    for pages, prompt, plens in [(6, 0, None), (2, 17, [529, 31, 1])]:
-        w = _small_sparse(batch=3 if plens else 2, pages=pages, prompt=prompt)
-        say("block index/score", pages, prompt, plens)
+    for pages, prompt, plens in [(6, 0, None), (2, 17, [529, 31, 1]), (9, 5, [1000, 0, 70, 33])]:
+        w = _small_sparse(batch=len(plens) if plens else 2, pages=pages, prompt=prompt, dtype=dtype,
+                          head_dim=head_dim)
+        say("block index/score", dtype, head_dim, pages, prompt, plens)
         sess = DecodeSession(w)
         host = HostMirror(w)
         if plens:
