@@ -209,7 +209,7 @@ int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route,
  * sparse step keeps the block scores on chip (no scores array).
  *   uocr_rswa_step: workspace and num_splits as for uocr_rswa_decode.
  *   uocr_srswa_step: one workgroup per unit; num_splits = waves per
- *   workgroup, 4 or 8 (0 = 8).                                              */
+ *   workgroup, 4, 8 or 16 (0 = 8).                                         */
 int uocr_rswa_step(const uocr_shape* shape, const void* q, const void* k_new,
                    const void* v_new, const void* k_prefix, const void* v_prefix,
                    const int32_t* prefix_len, void* k_ring, void* v_ring,

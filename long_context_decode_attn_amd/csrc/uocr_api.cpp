@@ -507,8 +507,8 @@ int uocr_srswa_step(const uocr_shape* shape, const uocr_route* route, const void
   if (sel_prob) ALIGN4(sel_prob, "sel_prob");
   if (overlap(t_gen_in, t_gen_out, (size_t)shape->batch * 4))
     return fail(UOCR_ERR_UNSUPPORTED, "%s: t_gen_out overlaps t_gen_in", fn);
-  if (num_splits != 0 && num_splits != 4 && num_splits != 8)
-    return fail(UOCR_ERR_SHAPE, "%s: num_splits %d is not 0, 4 or 8", fn, num_splits);
+  if (num_splits != 0 && num_splits != 4 && num_splits != 8 && num_splits != 16)
+    return fail(UOCR_ERR_SHAPE, "%s: num_splits %d is not 0, 4, 8 or 16", fn, num_splits);
   uocr::StepArgs a{};
   a.d.q = q;
   a.d.k_prefix = k_prefix;
@@ -522,7 +522,7 @@ int uocr_srswa_step(const uocr_shape* shape, const uocr_route* route, const void
   a.d.prefix_cap = shape->prefix_cap;
   a.d.window = shape->window;
   a.d.splits = 1;
-  a.d.waves = num_splits == 4 ? 4 : 8;
+  a.d.waves = num_splits != 0 ? num_splits : kSparseWaves;
   a.d.qscale = shape->scale * 1.4426950408889634f;
   a.d.topk = route->topk;
   a.k_new = k_new;

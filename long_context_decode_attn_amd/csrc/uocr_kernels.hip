@@ -399,40 +399,31 @@ __device__ __forceinline__ void wg_finish(State<Geo<DT, D>::E>& st, float (*lds_
     lds_ml[wave][1] = st.l;
   }
   __syncthreads();
-  if (wave != 0) return;
-  constexpr int DPL = D / 64;  // dimensions per lane in the merge
+  // every thread takes the common maximum, then output dimensions are dealt
+  // to the threads; each sums the W waves' weighted partials in wave order
+  // (a wave that saw no key has l = 0 and acc = 0 and adds exactly nothing)
   float M = kFloor;
   for (int w = 0; w < W; ++w) M = fmaxf(M, lds_ml[w][0]);
-  float L = 0.f, O[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) O[i] = 0.f;
-  for (int w = 0; w < W; ++w) {
-    const float l = lds_ml[w][1];
-    if (l == 0.f) continue;
-    const float f = fexp2(lds_ml[w][0] - M);
-    L = fmaf(f, l, L);
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) O[i] = fmaf(f, lds_o[w * D + lane * DPL + i], O[i]);
-  }
-  if (a.splits == 1) {
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    char* dst = static_cast<char*>(a.out) + (size_t)unit * G::ROWB;
-    if constexpr (DT == 0) {
-      float* d = reinterpret_cast<float*>(dst) + lane * DPL;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) d[i] = O[i] * inv;
-    } else {
-      uint16_t* d = reinterpret_cast<uint16_t*>(dst) + lane * DPL;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) d[i] = (uint16_t)bf16_bits(O[i] * inv);
+  for (int t = threadIdx.x; t < D; t += blockDim.x) {
+    float L = 0.f, O = 0.f;
+    for (int w = 0; w < W; ++w) {
+      const float f = fexp2(lds_ml[w][0] - M);
+      L = fmaf(f, lds_ml[w][1], L);
+      O = fmaf(f, lds_o[w * D + t], O);
     }
-    return;
+    if (a.splits == 1) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      char* dst = static_cast<char*>(a.out) + (size_t)unit * G::ROWB;
+      if constexpr (DT == 0)
+        reinterpret_cast<float*>(dst)[t] = O * inv;
+      else
+        reinterpret_cast<uint16_t*>(dst)[t] = (uint16_t)bf16_bits(O * inv);
+    } else {
+      const size_t part = (size_t)unit * a.splits + split;
+      if (t == 0) *reinterpret_cast<float2*>(a.part_ml + part * 2) = make_float2(M, L);
+      a.part_o[part * D + t] = O;
+    }
   }
-  const size_t part = (size_t)unit * a.splits + split;
-  if (lane == 0) *reinterpret_cast<float2*>(a.part_ml + part * 2) = make_float2(M, L);
-  float* po = a.part_o + part * D + lane * DPL;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) po[i] = O[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -849,6 +840,12 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 constexpr int kPairMax = 256;  // largest candidate set ranked pairwise
 constexpr int kWaveBlocks = 16; // blocks per lane on the one-wave path (nb <= 1024)
 
+struct PairBuf {  // pairwise ranking (16-byte aligned rows)
+  float val[kPairMax + 4];
+  int idx[kPairMax + 4];
+  int rank[kPairMax + 4];
+};
+
 template <int NT>
 struct __attribute__((aligned(16))) TopkSmem {
   uint32_t hist[256];
@@ -859,11 +856,7 @@ struct __attribute__((aligned(16))) TopkSmem {
   double tau;
   union alignas(16) {
     double cand[kMaxBlocks];  // sorted path
-    struct {                  // pairwise path (16-byte aligned rows)
-      float val[kPairMax + 4];
-      int idx[kPairMax + 4];
-      int rank[kPairMax + 4];
-    } a;
+    PairBuf a;                // pairwise paths
   };
 };
 
@@ -909,6 +902,131 @@ struct NoOverlap {
   __device__ void operator()() const {}
 };
 
+// One-wave routing for nb <= 64 * NS blocks (see entmax_topk_block).  Returns
+// false, having written nothing, when the candidate set exceeds 64 blocks.
+template <int NS>
+__device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32_t* o_idx, float* o_prob,
+                                           float* o_bias, int* l_idx, float* l_bias, PairBuf& pb) {
+  const int lane = threadIdx.x & 63;
+  // the routing is the critical path of the step: let this wave win the
+  // issue arbitration against the waves attending over the window
+  __builtin_amdgcn_s_setprio(3);
+  float sv[NS];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < NS; ++e) {
+    const int j = e * 64 + lane;
+    sv[e] = j < nb ? s[j] : -INFINITY;
+    lmax = fmaxf(lmax, sv[e]);
+  }
+  const float smax = wave_max(lmax);
+  const double dmax = (double)smax;
+  float dv[NS];
+#pragma unroll
+  for (int e = 0; e < NS; ++e) dv[e] = smax - sv[e];  // +inf past nb
+  float T = 4.f;
+  int nA = 0;
+  for (int it = 0; it < 130; ++it) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < NS; ++e) c += dv[e] < T ? 1 : 0;
+    nA = wave_sum(c);
+    if (nA >= kk) break;
+    T = T * 2.f;  // reaches +inf, where every finite d counts
+  }
+  if (nA <= 64) {
+    // ordered compaction of A (and of the entmax candidates) by ballots
+    int base = 0, cbase = 0;
+#pragma unroll
+    for (int e = 0; e < NS; ++e) {
+      const bool in = dv[e] < T;
+      const bool cd = ((double)sv[e] - dmax) * 0.5 > -1.0;
+      const uint64_t m = __ballot(in);
+      const uint64_t mc = __ballot(cd);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const int cbelow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
+      if (in) {
+        pb.val[base + below] = sv[e];
+        pb.idx[base + below] = e * 64 + lane;
+      }
+      if (cd) pb.rank[cbase + cbelow] = __float_as_int(sv[e]);  // candidate scores
+      base += __popcll(m);
+      cbase += __popcll(mc);
+    }
+    const int nC = cbase;
+    const int nA4 = (nA + 3) & ~3, nC4 = (nC + 3) & ~3;
+    if (lane < nA4 - nA) {
+      pb.val[nA + lane] = -INFINITY;  // ranks below every block, never >= a real score
+      pb.idx[nA + lane] = 0x7fffffff;
+    }
+    if (lane < nC4 - nC) pb.rank[nC + lane] = __float_as_int(-INFINITY);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bool mine = lane < nA;
+    const float si = mine ? pb.val[lane] : -INFINITY;
+    const int ii = mine ? pb.idx[lane] : 0x7fffffff;
+    const double vi = ((double)si - dmax) * 0.5;
+    const bool cand = mine && vi > -1.0;
+    const float4* val4 = reinterpret_cast<const float4*>(pb.val);
+    const int4* idx4 = reinterpret_cast<const int4*>(pb.idx);
+    int rank = 0;
+#pragma unroll 4
+    for (int k4 = 0; k4 < nA4 / 4; ++k4) {
+      const float4 sk = val4[k4];
+      const int4 ik = idx4[k4];
+      rank += (sk.x > si || (sk.x == si && ik.x < ii)) + (sk.y > si || (sk.y == si && ik.y < ii)) +
+              (sk.z > si || (sk.z == si && ik.z < ii)) + (sk.w > si || (sk.w == si && ik.w < ii));
+    }
+    const float4* cv4 = reinterpret_cast<const float4*>(pb.rank);
+    int r = 0;
+    double s1 = 0.0, s2 = 0.0;
+    for (int k4 = 0; k4 < nC4 / 4; ++k4) {
+      const float4 c4 = cv4[k4];
+      const float ck[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (ck[k] >= si) {
+          const double vk = ((double)ck[k] - dmax) * 0.5;
+          ++r;
+          s1 += vk;
+          s2 += vk * vk;
+        }
+      }
+    }
+    int rr = 0;
+    double tl = 0.0;
+    if (cand) {
+      const double mu = s1 / r;
+      const double ss = s2 - s1 * mu;
+      tl = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
+      rr = tl <= vi ? r : 0;
+    }
+    const int rstar = wave_max(rr);
+    const uint64_t win = __ballot(rr == rstar && rr > 0);
+    const double tau = readlane_d(tl, __ffsll((unsigned long long)win) - 1);
+    const bool sel = mine && rank < kk;
+    const uint64_t sm_ = __ballot(sel);
+    if (sel) {
+      const int at = __builtin_amdgcn_mbcnt_hi((uint32_t)(sm_ >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)sm_, 0u));
+      const double dd = vi - tau;
+      const float p = dd > 0.0 ? (float)(dd * dd) : 0.f;
+      const float bias = p > 0.f ? logf(p) : -INFINITY;
+      o_idx[at] = ii;
+      if (o_prob) o_prob[at] = p;
+      o_bias[at] = bias;
+      if (l_idx) {
+        l_idx[at] = ii;
+        l_bias[at] = bias;
+      }
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+  return nA <= 64;
+}
+
 // Routing of one unit from its nb scores `s` (global or LDS).  Writes topk
 // entries of o_idx / o_prob (may be null) / o_bias and, when l_idx is not
 // null, the same indices and biases to l_idx / l_bias.  Every thread of the
@@ -951,123 +1069,13 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
   if (nb <= 64 * kWaveBlocks) {
     if (wave != 0) others();
     if (wave == 0) {
-      // the routing is the critical path of the step: let this wave win the
-      // issue arbitration against the waves attending over the window
-      __builtin_amdgcn_s_setprio(3);
-      float sv[kWaveBlocks];
-      float lmax = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < kWaveBlocks; ++e) {
-        const int j = e * 64 + lane;
-        sv[e] = j < nb ? s[j] : -INFINITY;
-        lmax = fmaxf(lmax, sv[e]);
-      }
-      const float smax = wave_max(lmax);
-      const double dmax = (double)smax;
-      float dv[kWaveBlocks];
-#pragma unroll
-      for (int e = 0; e < kWaveBlocks; ++e) dv[e] = smax - sv[e];  // +inf past nb
-      float T = 4.f;
-      int nA = 0;
-      for (int it = 0; it < 130; ++it) {
-        int c = 0;
-#pragma unroll
-        for (int e = 0; e < kWaveBlocks; ++e) c += dv[e] < T ? 1 : 0;
-        nA = wave_sum(c);
-        if (nA >= kk) break;
-        T = T * 2.f;  // reaches +inf, where every finite d counts
-      }
-      if (nA <= 64) {
-        // ordered compaction of A (and of the entmax candidates) by ballots
-        int base = 0, cbase = 0;
-#pragma unroll
-        for (int e = 0; e < kWaveBlocks; ++e) {
-          const bool in = dv[e] < T;
-          const bool cd = ((double)sv[e] - dmax) * 0.5 > -1.0;
-          const uint64_t m = __ballot(in);
-          const uint64_t mc = __ballot(cd);
-          const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          const int cbelow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
-          if (in) {
-            sm.a.val[base + below] = sv[e];
-            sm.a.idx[base + below] = e * 64 + lane;
-          }
-          if (cd) sm.a.rank[cbase + cbelow] = __float_as_int(sv[e]);  // candidate scores
-          base += __popcll(m);
-          cbase += __popcll(mc);
-        }
-        const int nC = cbase;
-        const int nA4 = (nA + 3) & ~3, nC4 = (nC + 3) & ~3;
-        if (lane < nA4 - nA) {
-          sm.a.val[nA + lane] = -INFINITY;  // ranks below every block, never >= a real score
-          sm.a.idx[nA + lane] = 0x7fffffff;
-        }
-        if (lane < nC4 - nC) sm.a.rank[nC + lane] = __float_as_int(-INFINITY);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const bool mine = lane < nA;
-        const float si = mine ? sm.a.val[lane] : -INFINITY;
-        const int ii = mine ? sm.a.idx[lane] : 0x7fffffff;
-        const double vi = ((double)si - dmax) * 0.5;
-        const bool cand = mine && vi > -1.0;
-        const float4* val4 = reinterpret_cast<const float4*>(sm.a.val);
-        const int4* idx4 = reinterpret_cast<const int4*>(sm.a.idx);
-        int rank = 0;
-#pragma unroll 4
-        for (int k4 = 0; k4 < nA4 / 4; ++k4) {
-          const float4 sk = val4[k4];
-          const int4 ik = idx4[k4];
-          rank += (sk.x > si || (sk.x == si && ik.x < ii)) + (sk.y > si || (sk.y == si && ik.y < ii)) +
-                  (sk.z > si || (sk.z == si && ik.z < ii)) + (sk.w > si || (sk.w == si && ik.w < ii));
-        }
-        const float4* cv4 = reinterpret_cast<const float4*>(sm.a.rank);
-        int r = 0;
-        double s1 = 0.0, s2 = 0.0;
-        for (int k4 = 0; k4 < nC4 / 4; ++k4) {
-          const float4 c4 = cv4[k4];
-          const float ck[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            if (ck[k] >= si) {
-              const double vk = ((double)ck[k] - dmax) * 0.5;
-              ++r;
-              s1 += vk;
-              s2 += vk * vk;
-            }
-          }
-        }
-        int rr = 0;
-        double tl = 0.0;
-        if (cand) {
-          const double mu = s1 / r;
-          const double ss = s2 - s1 * mu;
-          tl = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
-          rr = tl <= vi ? r : 0;
-        }
-        const int rstar = wave_max(rr);
-        const uint64_t win = __ballot(rr == rstar && rr > 0);
-        const double tau = readlane_d(tl, __ffsll((unsigned long long)win) - 1);
-        const bool sel = mine && rank < kk;
-        const uint64_t sm_ = __ballot(sel);
-        if (sel) {
-          const int at = __builtin_amdgcn_mbcnt_hi((uint32_t)(sm_ >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)sm_, 0u));
-          const double dd = vi - tau;
-          const float p = dd > 0.0 ? (float)(dd * dd) : 0.f;
-          const float bias = p > 0.f ? logf(p) : -INFINITY;
-          o_idx[at] = ii;
-          if (o_prob) o_prob[at] = p;
-          o_bias[at] = bias;
-          if (l_idx) {
-            l_idx[at] = ii;
-            l_bias[at] = bias;
-          }
-        }
-      }
-      if (lane == 0) sm.digit = nA <= 64 ? 1u : 0u;
-      __builtin_amdgcn_s_setprio(0);
+      bool ok;
+      if (nb <= 64) ok = wave_route<1>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
+      else if (nb <= 128) ok = wave_route<2>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
+      else if (nb <= 256) ok = wave_route<4>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
+      else if (nb <= 512) ok = wave_route<8>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
+      else ok = wave_route<16>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
+      if (lane == 0) sm.digit = ok ? 1u : 0u;
     }
     __syncthreads();
     const bool done = sm.digit == 1u;
@@ -1430,7 +1438,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
 //      from k_new / v_new, so no wave waits for the ring write);
 //   4. attend over the live selected blocks; merge the waves through LDS.
 template <int DT, int D, int NT, bool STREAM>
-__global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a) {
+__global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a) {
   using G = Geo<DT, D>;
   constexpr int W = NT / 64;
   constexpr int SL = NT / kIdxDim;  // slices of D in the q_idx product
@@ -1438,7 +1446,7 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a
   constexpr int RPP = NT / 8;       // block keys per pass (8 lanes per key)
   __shared__ float s_scores[kMaxBlocks];
   __shared__ double s_red[SL][kIdxDim];
-  __shared__ double s_qidx[kIdxDim];
+  __shared__ __attribute__((aligned(16))) double s_qidx[kIdxDim];
   __shared__ TopkSmem<NT> tsm;
   __shared__ int l_idx[kMaxTopk];
   __shared__ float l_bias[kMaxTopk];
@@ -1464,10 +1472,29 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a
   }
   if (h == 0 && tid == 0) a.t_gen_out[b] = t + 1;
 
-  // first two batches of block keys, in flight during the window attention
+  // q_idx partial sums: the loads of P and q go out first, so that they are
+  // not queued behind the block keys
+  const int i_q = tid % kIdxDim, sl_q = tid / kIdxDim;
+  constexpr int DPS = D / SL;
+  float pv[DPS], qv_[DPS];
+  {
+    const char* qrow = static_cast<const char*>(d.q) + (size_t)unit * G::ROWB;
+#pragma unroll
+    for (int k = 0; k < DPS; ++k) {
+      const int dd = sl_q * DPS + k;
+      pv[k] = a.proj[dd * kIdxDim + i_q];
+      if constexpr (DT == 0)
+        qv_[k] = reinterpret_cast<const float*>(qrow)[dd];
+      else
+        qv_[k] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[dd] << 16);
+    }
+  }
+
+  // the first two batches of block keys (rows < nb_cap: no wait for
+  // prefix_len), in flight while q_idx is formed
   const int kr = tid / 8, kc = tid % 8;
   const float* K = a.kbar + (size_t)unit * a.nb_cap * kIdxDim + kc * 4;
-  auto load_keys = [&](float4 (&dst)[KB], int jb) {  // rows < nb_cap: no wait for prefix_len
+  auto load_keys = [&](float4 (&dst)[KB], int jb) {
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int j = jb + u * RPP + kr;
@@ -1480,23 +1507,11 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a
   load_keys(kvA, 0);
   load_keys(kvB, RPP * KB);
 
-  // q_idx partial sums
   {
-    const int i = tid % kIdxDim, sl = tid / kIdxDim;
-    constexpr int DPS = D / SL;
-    const char* qrow = static_cast<const char*>(d.q) + (size_t)unit * G::ROWB;
     double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < DPS; ++k) {
-      const int dd = sl * DPS + k;
-      float qd;
-      if constexpr (DT == 0)
-        qd = reinterpret_cast<const float*>(qrow)[dd];
-      else
-        qd = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[dd] << 16);
-      acc += (double)a.proj[dd * kIdxDim + i] * (double)qd;
-    }
-    s_red[sl][i] = acc;
+    for (int k = 0; k < DPS; ++k) acc += (double)pv[k] * (double)qv_[k];
+    s_red[sl_q][i_q] = acc;
   }
 
   float q[G::E];
@@ -1531,9 +1546,9 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a
     constexpr int BATCH = RPP * KB;
     for (int jb = 0; jb < nb; jb += 2 * BATCH) {
       score(kvA, jb);
-      if (jb + 2 * BATCH < a.nb_cap) load_keys(kvA, jb + 2 * BATCH);
+      if (jb + 2 * BATCH < nb) load_keys(kvA, jb + 2 * BATCH);
       score(kvB, jb + BATCH);
-      if (jb + 3 * BATCH < a.nb_cap) load_keys(kvB, jb + 3 * BATCH);
+      if (jb + 3 * BATCH < nb) load_keys(kvB, jb + 3 * BATCH);
     }
   }
   __syncthreads();
@@ -1560,7 +1575,8 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a
                         a.sel_bias + so, l_idx, l_bias, tsm, window);
   __syncthreads();
 
-  // live selected blocks, dealt round-robin to the waves
+  // live selected blocks: with fewer of them than waves each block is cut
+  // into cpb chunks of 32 / cpb rows, so that every wave has loads in flight
   int idx = -1;
   float bias = 0.f;
   bool live = false;
@@ -1571,17 +1587,22 @@ __global__ __launch_bounds__(NT, NT == 512 ? 4 : 3) void k_srswa_step(StepArgs a
   }
   const uint64_t mask = __ballot(live);
   const int n_live = __popcll(mask);
-  for (int tk = wave; tk < n_live; tk += W) {
+  int cpb = 1;
+  while (2 * cpb * n_live <= W && 2 * cpb * G::RPL <= kBlock) cpb *= 2;
+  const int rpc = kBlock / cpb;
+  for (int task = wave; task < n_live * cpb; task += W) {
+    const int tk = task / cpb, sub = task - tk * cpb;
     uint64_t mm = mask;
     for (int i = 0; i < tk; ++i) mm &= mm - 1;
     const int sl = __ffsll((unsigned long long)mm) - 1;
     const int j = __shfl(idx, sl);
     const float bj = __shfl(bias, sl);
-    const int r0 = j * kBlock;
+    const int r0 = j * kBlock + sub * rpc;
+    const int nr = min(rpc, m - r0);
+    if (nr <= 0) continue;
     const size_t base = ((size_t)unit * d.prefix_cap + r0) * G::ROWB + cb;
     attend_range<DT, D, G::U, STREAM>(static_cast<const char*>(d.k_prefix) + base,
-                                      static_cast<const char*>(d.v_prefix) + base, min(kBlock, m - r0), bj * kLog2e, q,
-                                      st, grp);
+                                      static_cast<const char*>(d.v_prefix) + base, nr, bj * kLog2e, q, st, grp);
   }
   wg_finish<DT, D>(st, lds_ml, lds_o, d, unit, 0);
 }
@@ -1718,7 +1739,13 @@ hipError_t launch_srswa_step(int dtype, int head_dim, const StepArgs& a, hipStre
     if (stream) k_srswa_step<DT_, D_, NT_, true><<<grid, NT_, 0, s>>>(a);             \
     else k_srswa_step<DT_, D_, NT_, false><<<grid, NT_, 0, s>>>(a);                   \
   } while (0)
-  if (a.d.waves == 8) {
+  if (a.d.waves == 16) {
+    if (dtype == 0 && head_dim == 64) UOCR_STEP(0, 64, 1024);
+    else if (dtype == 0 && head_dim == 128) UOCR_STEP(0, 128, 1024);
+    else if (dtype == 1 && head_dim == 64) UOCR_STEP(1, 64, 1024);
+    else if (dtype == 1 && head_dim == 128) UOCR_STEP(1, 128, 1024);
+    else return hipErrorInvalidValue;
+  } else if (a.d.waves == 8) {
     if (dtype == 0 && head_dim == 64) UOCR_STEP(0, 64, 512);
     else if (dtype == 0 && head_dim == 128) UOCR_STEP(0, 128, 512);
     else if (dtype == 1 && head_dim == 64) UOCR_STEP(1, 64, 512);

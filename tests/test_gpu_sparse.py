@@ -180,7 +180,7 @@ def test_srswa_decode_given_selection(live, with_bias):
 
 
 @pytest.mark.parametrize("num_splits,fused", [(0, False), (1, False), (3, False), (8, False),
-                                              (0, True), (4, True), (8, True)])
+                                              (0, True), (4, True), (8, True), (16, True)])
 def test_srswa_pipeline_small(num_splits, fused):
     """append -> score -> entmax top-k -> sparse decode for several steps,
     selections and outputs against the oracle's own routing."""
