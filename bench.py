@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--workload", default="srswa-40p-b32")
     ap.add_argument("--layers", type=int, default=12, help="independent per-layer states cycled by the steps")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--t0", type=int, default=None,
+                    help="generated tokens before the first step (default: the workload's; for flatness runs)")
     ap.add_argument("--mode", choices=["fused", "separate"], default="fused",
                     help="fused: one uocr_*_step launch per step; separate: one launch per row")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
@@ -177,6 +179,8 @@ def main():
     U.load_library()
     torch.cuda.set_device(0)
     w = S.WORKLOADS[args.workload]
+    if args.t0 is not None:
+        w = w.replace(t0=args.t0)
     t_setup = time.perf_counter()
     fused = args.mode == "fused"
     base = DecodeSession(w, num_splits=args.num_splits, fused=fused)
@@ -317,10 +321,11 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
-                   "prefix_tokens": w.prefix_len, "pages": w.pages, "window": w.window,
+                   "prefix_tokens": w.prefix_len, "pages": w.pages, "window": w.window, "t0": w.t0,
                    "sparse": w.sparse, "topk": w.topk if w.sparse else None,
                    "block": w.block if w.sparse else None, "layers_cycled": len(layers),
-                   "splits": (U.uocr_srswa_splits(base.shape, base.route, args.num_splits) if w.sparse
+                   "splits": ((args.num_splits or 8) if w.sparse and fused
+                              else U.uocr_srswa_splits(base.shape, base.route, args.num_splits) if w.sparse
                               else U.uocr_rswa_splits(base.shape, args.num_splits)),
                    "mode": args.mode, "accumulate": "f32 attention, f64 routing",
                    "parallelism": "single-gpu"},

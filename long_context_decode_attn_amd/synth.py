@@ -77,7 +77,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads.  Names say what they are; sizes are in the fields.
+# The workloads.  Names say what they are; sizes are in the fields.
 WORKLOADS: Dict[str, Workload] = {
     w.name: w for w in [
         # dense, CPU-sized, fp32: 2 pages + 16 prompt tokens, ring starts
@@ -90,6 +90,12 @@ WORKLOADS: Dict[str, Workload] = {
         # dense, high concurrency, short context: 1 page + 32 prompt
         Workload("dense-1p-b512", batch=512, heads=10, head_dim=128, dtype="bf16",
                  pages=1, prompt=32, t0=128, steps=1000, seed=1003),
+        # dense companions of the two SR-SWA shapes: R-SWA over the whole
+        # 40-page / 125-page prefix plus the window
+        Workload("dense-40p-b32", batch=32, heads=10, head_dim=128, dtype="bf16",
+                 pages=40, prompt=0, t0=128, steps=1000, seed=1006),
+        Workload("dense-125p-b8", batch=8, heads=10, head_dim=128, dtype="bf16",
+                 pages=125, prompt=0, t0=128, steps=2048, seed=1007),
         # SR-SWA at 40 pages: 320 blocks, 16 planted per sequence
         Workload("srswa-40p-b32", batch=32, heads=10, head_dim=128, dtype="bf16",
                  pages=40, prompt=0, t0=128, steps=1000, seed=1004, sparse=True,

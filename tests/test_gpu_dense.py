@@ -125,7 +125,8 @@ def test_dense_empty_key_set_gives_zero():
 
 
 @pytest.mark.parametrize("name,fused", [("dense-10p-b64", False), ("dense-1p-b512", False),
-                                        ("dense-10p-b64", True), ("dense-1p-b512", True)])
+                                        ("dense-10p-b64", True), ("dense-1p-b512", True),
+                                        ("dense-40p-b32", True), ("dense-125p-b8", True)])
 def test_dense_full_size_sampled(name, fused):
     """Full-size dense workloads in the benchmark's launch configuration:
     every output finite, 32 sampled units per step checked."""
