@@ -39,10 +39,12 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("87d6d8af75a9148e", 45059883, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("87d6d8af75a9148e", 18760819, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("87d6d8af75a9148e", 892436856, 1720756),
-    ("uocr_rswa_step", "dense-1p-b512"): ("87d6d8af75a9148e", 1092080498, 3940462),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("466dbe1b612e8206", 45162633, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("466dbe1b612e8206", 18867663, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("466dbe1b612e8206", 892439280, 1720749),
+    ("uocr_rswa_step", "dense-1p-b512"): ("466dbe1b612e8206", 1092083661, 3940444),
+    ("uocr_rswa_step", "dense-40p-b32"): ("466dbe1b612e8206", 1699637165, 1383423),
+    ("uocr_rswa_step", "dense-125p-b8"): ("466dbe1b612e8206", 1316342296, 1172862),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
@@ -343,6 +345,11 @@ def main():
         result["routing"] = {"live_blocks_per_unit": round(live / w.units, 3),
                              "index_build_ms_per_layer": round(idx_ms, 4),
                              "index_build_gbs": round(index_bytes(w) / (idx_ms * 1e-3) / 1e9, 1)}
+        # the same step time priced as if every selected block were read (the
+        # achieved figure above counts only blocks with p > 0, the ones read)
+        full = sum(algorithmic_bytes(w, None).values()) - (2 * w.units * w.n_blocks * 4 if fused else 0)
+        result["routing"]["all_selected_blocks_bytes"] = full
+        result["routing"]["all_selected_blocks_gbs"] = round(full / (ms_per_step * 1e-3) / 1e9, 1)
     result["setup_s"] = round(setup_s, 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
