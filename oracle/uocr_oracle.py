@@ -342,6 +342,41 @@ def srswa_decode(q, k_prefix, v_prefix, prefix_len, sel_idx, sel_bias,
 
 
 # ============================================================================
+# Prefill-side routing   ([Unlimited OCR Works README mirror] SGLang server
+# section, notes on the memory knobs: the prefill holds a temporary score
+# tensor of about [tokens, context/32], one score per (prefill token, block))
+# ============================================================================
+# Readings (the page gives only that tensor's shape): every query of a prefill
+# chunk is routed the way a decode query is (scores, 1.5-entmax, top-k, log
+# bias), over the prefix blocks it may see causally -- the blocks all of whose
+# prefix tokens come before the query's position.  A block that still holds
+# the query or a later token is left to the local window.
+
+def visible_blocks(t: int, m: int, block: int = 32) -> int:
+    """Prefix blocks a query at absolute position t may route to: block j
+    (tokens [32j, min(32j + 32, m))) counts when every one of its tokens is
+    at a position < t.  Blocks are contiguous from 0, so this is a count."""
+    return sum(1 for lo, hi in block_ranges(m, block) if hi <= t)
+
+
+def prefill_route_unit(q_rows: np.ndarray, q_pos: int, proj: np.ndarray, kbar: np.ndarray,
+                       m: int, k: int, block: int = 32):
+    """Routing of the Tq queries of one unit's prefill chunk: query i sits at
+    position q_pos + i and is routed over its visible blocks from its scores
+    rounded to float32.  q_rows [Tq][D], kbar [nb][d].
+    Returns idx int32 [Tq][k], prob [Tq][k], bias [Tq][k]."""
+    Tq = len(q_rows)
+    idx = np.full((Tq, k), -1, dtype=np.int32)
+    prob = np.zeros((Tq, k), dtype=F64)
+    bias = np.full((Tq, k), NEG_INF, dtype=F64)
+    for i in range(Tq):
+        nbv = visible_blocks(q_pos + i, m, block)
+        s32 = as_f32(block_scores(q_rows[i], proj, kbar[:nbv]))
+        idx[i], prob[i], bias[i] = route_unit(s32, k)
+    return idx, prob, bias
+
+
+# ============================================================================
 # Whole routing of a batch, and the certified-gap rule for near-ties
 # ============================================================================
 def route(q, k_prefix, prefix_len, proj, k: int, block: int = 32):

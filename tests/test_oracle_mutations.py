@@ -131,3 +131,14 @@ def test_srswa_missing_window_is_caught():
     def srswa_unit(q, K, V, m, sel, bias, wk, wv, scale, block=32):
         return O.srswa_unit(q, K, V, m, sel, bias, wk[:0], wv[:0], scale, block)
     _fails(T.check_srswa, srswa_unit=srswa_unit)
+
+
+def test_prefill_visibility_including_the_query_block_is_caught():
+    _fails(T.check_prefill_route,
+           visible_blocks=lambda t, m, block=32: sum(1 for lo, hi in O.block_ranges(m, block) if lo < t))
+
+
+def test_prefill_route_ignoring_chunk_position_is_caught():
+    def prefill_route_unit(q, q_pos, P, kbar, m, k, block=32):
+        return O.prefill_route_unit(q, 0, P, kbar, m, k, block)
+    _fails(T.check_prefill_route, prefill_route_unit=prefill_route_unit)

@@ -407,3 +407,61 @@ def test_ambiguity_rule_flags_only_near_ties():
     assert not O.ambiguous_boundary(s, eps, 1)
     assert not O.ambiguous_boundary(s, eps, 3)
     assert not O.ambiguous_boundary(s, eps, 4)    # fewer than k+1 blocks
+
+
+# ----------------------------------------------------------------------------
+# prefill-side routing: causal visibility and per-query routing
+# ----------------------------------------------------------------------------
+def _visible_by_tokens(t, m, block=32):
+    """Count the blocks none of whose prefix tokens is at a position >= t,
+    token by token."""
+    late = set()
+    for p in range(m):
+        if p >= t:
+            late.add(p // block)
+    n_blocks = (m + block - 1) // block
+    return sum(1 for b in range(n_blocks) if b not in late)
+
+
+def _route_by_enumeration(s, k):
+    """Top-k by a full sort of (-score, index) and 1.5-entmax by enumerating
+    every support set."""
+    if len(s) == 0:
+        return [], np.zeros(0)
+    order = sorted(range(len(s)), key=lambda j: (-float(s[j]), j))
+    return sorted(order[:min(k, len(s))]), O.entmax15_bruteforce(s)
+
+
+def check_prefill_route(visible_blocks=O.visible_blocks, prefill_route_unit=O.prefill_route_unit):
+    for m in [0, 1, 31, 32, 33, 100, 128, 130]:
+        for t in range(-2, m + 70):
+            assert visible_blocks(t, m) == _visible_by_tokens(t, m), (t, m)
+    rng = np.random.default_rng(17)
+    D, d, k = 8, 4, 3
+    P = rng.normal(size=(D, d))
+    for m, q_pos, Tq in [(300, 0, 40), (300, 250, 70), (40, 30, 12), (64, 64, 3)]:
+        nb = (m + 31) // 32
+        kbar = O.as_f32(rng.normal(size=(nb, d)))
+        q = rng.normal(size=(Tq, D)) * 3.0
+        idx, prob, bias = prefill_route_unit(q, q_pos, P, kbar, m, k)
+        for i in range(Tq):
+            t = q_pos + i
+            nbv = _visible_by_tokens(t, m)
+            s = np.array([float(np.float32(sum(float(q[i] @ P[:, c]) * kbar[j, c] for c in range(d))))
+                          for j in range(nbv)])
+            sel, p = _route_by_enumeration(s, k)
+            want = np.full(k, -1)
+            want[:len(sel)] = sel
+            assert np.array_equal(idx[i], want), (m, q_pos, i)
+            for a, j in enumerate(sel):
+                assert abs(prob[i, a] - p[j]) < 1e-12
+                assert (bias[i, a] == -math.inf) if p[j] == 0 else abs(bias[i, a] - math.log(p[j])) < 1e-12
+                assert min(32 * (j + 1), m) <= t          # no token at or after the query
+            assert (prob[i, len(sel):] == 0).all() and np.isneginf(bias[i, len(sel):]).all()
+            if t >= m:   # after the prefix: the routing of a decode query
+                d_idx, d_prob, _ = O.route_unit(O.as_f32(O.block_scores(q[i], P, kbar)), k)
+                assert np.array_equal(idx[i], d_idx) and np.allclose(prob[i], d_prob, atol=1e-12)
+
+
+def test_prefill_route_causal_and_enumerated():
+    check_prefill_route()
