@@ -178,6 +178,33 @@ int uocr_entmax15_topk(const uocr_shape* shape, const uocr_route* route,
                        void* stream);
 
 /* ---------------------------------------------------------------------------
+ * uocr_prefill_route -- routing of a prefill chunk: every query of the chunk
+ * routed over the prefix blocks it may see.
+ * [Unlimited OCR Works README mirror (git.zoyku.com), SGLang server section,
+ * notes on the memory knobs: the prefill holds a temporary score tensor of
+ * about [tokens, context/32]; the routing of each query is the one of
+ * uocr_block_score + uocr_entmax15_topk above.]
+ *   q        [B][H][tq][D] in shape->dtype: the chunk's queries;
+ *   q_pos    [B] int32 (device): position of query 0 of the chunk; query i
+ *            sits at q_pos[b] + i;
+ *   kbar_idx [B][H][nb_cap][32] from uocr_block_index_build.
+ *   Query i sees the blocks all of whose prefix tokens come before its
+ *   position: ceil(m/32) blocks once q_pos[b] + i >= m, otherwise
+ *   floor((q_pos[b] + i)/32) (none for a negative position).  Over those it is
+ *   routed exactly as uocr_entmax15_topk routes a decode query (fp64 scores
+ *   rounded once to fp32, 1.5-entmax, top-k by (score desc, index asc),
+ *   ascending index order, bias = ln p).  Outputs sel_idx / sel_prob /
+ *   sel_bias [B][H][tq][topk] (sel_prob may be NULL); entries past
+ *   min(topk, visible blocks) are idx -1, prob 0, bias -inf.
+ *   0 <= tq <= 2^20 and B*H*tq*topk < 2^31 (else UOCR_ERR_SHAPE); tq = 0
+ *   does nothing.  Two launches on `stream`; the caller owns every buffer. */
+int uocr_prefill_route(const uocr_shape* shape, const uocr_route* route,
+                       const void* q, int32_t tq, const int32_t* q_pos,
+                       const float* proj, const float* kbar_idx,
+                       const int32_t* prefix_len, int32_t* sel_idx,
+                       float* sel_prob, float* sel_bias, void* stream);
+
+/* ---------------------------------------------------------------------------
  * uocr_srswa_decode -- SR-SWA decode: selected blocks + window, log bias.
  * [nxmr.cn/news/162408 "稀疏路由" step 4 and "环形缓冲"; 16 x 32 = 512
  * reference tokens per query.]

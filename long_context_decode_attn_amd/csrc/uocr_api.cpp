@@ -109,6 +109,7 @@ size_t ws_bytes_for(int units, int splits, int head_dim) {
 
 constexpr int kDenseWaves = 4;    // waves per workgroup of the dense decode
 constexpr int kSparseWaves = 8;   // default waves per unit of the sparse decode
+constexpr int kMaxPrefillQueries = 1 << 20;  // queries per unit in one prefill routing call
 
 // Dense split geometry: workgroups per unit and keys per workgroup for the
 // virtual key sequence of prefix_cap + window keys.
@@ -330,6 +331,43 @@ int uocr_entmax15_topk(const uocr_shape* shape, const uocr_route* route, const f
   uocr::TopkArgs a{scores, prefix_len, sel_idx, sel_prob, sel_bias, units_of(shape),
                    shape->heads, shape->prefix_cap, nb_cap_of(shape), route->topk};
   return hip_status(uocr::launch_entmax_topk(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int uocr_prefill_route(const uocr_shape* shape, const uocr_route* route, const void* q, int32_t tq,
+                       const int32_t* q_pos, const float* proj, const float* kbar_idx,
+                       const int32_t* prefix_len, int32_t* sel_idx, float* sel_prob, float* sel_bias,
+                       void* stream) {
+  const char* fn = "uocr_prefill_route";
+  CHECK(check_shape(shape, fn));
+  CHECK(check_route(shape, route, fn));
+  if (tq < 0 || tq > kMaxPrefillQueries)
+    return fail(UOCR_ERR_SHAPE, "%s: tq %d outside [0, %d]", fn, tq, kMaxPrefillQueries);
+  if ((long long)units_of(shape) * tq * route->topk > (1ll << 31) - 1)
+    return fail(UOCR_ERR_SHAPE, "%s: units x tq x topk exceeds 2^31 - 1", fn);
+  if (tq == 0) return ok();
+  NEED(q, "q");
+  NEED(q_pos, "q_pos");
+  NEED(proj, "proj");
+  NEED(prefix_len, "prefix_len");
+  NEED(sel_idx, "sel_idx");
+  NEED(sel_bias, "sel_bias");
+  ALIGN16(q, "q");
+  ALIGN4(q_pos, "q_pos");
+  ALIGN4(proj, "proj");
+  ALIGN4(prefix_len, "prefix_len");
+  ALIGN4(sel_idx, "sel_idx");
+  ALIGN4(sel_bias, "sel_bias");
+  if (sel_prob) ALIGN4(sel_prob, "sel_prob");
+  const int nb_cap = nb_cap_of(shape);
+  if (nb_cap > 0) {
+    NEED(kbar_idx, "kbar_idx");
+    ALIGN16(kbar_idx, "kbar_idx");
+  }
+  uocr::PrefillArgs a{q, q_pos, proj, kbar_idx, prefix_len, sel_idx, sel_prob, sel_bias, units_of(shape),
+                      shape->heads, shape->prefix_cap, nb_cap, route->topk, tq,
+                      uocr::prefill_queries_per_wg(nb_cap)};
+  return hip_status(uocr::launch_prefill_route(shape->dtype, shape->head_dim, a,
+                                               static_cast<hipStream_t>(stream)), fn);
 }
 
 int32_t uocr_srswa_splits(const uocr_shape* shape, const uocr_route* route, int32_t num_splits) {

@@ -66,6 +66,19 @@ struct TopkArgs {
   int units, heads, prefix_cap, nb_cap, topk;
 };
 
+// Prefill-side routing of a chunk of tq queries per unit.
+struct PrefillArgs {
+  const void* q;          // [units][tq][D]
+  const int32_t* q_pos;   // [batch] position of query 0 of the chunk
+  const float* proj;      // [D][32]
+  const float* kbar;      // [units][nb_cap][32]
+  const int32_t* prefix_len;
+  int32_t* sel_idx;       // [units][tq][topk]
+  float* sel_prob;        // may be null
+  float* sel_bias;
+  int units, heads, prefix_cap, nb_cap, topk, tq, qt;
+};
+
 // A fused decode step: DecodeArgs plus the new token, the double-buffered
 // generated-token counts and (SR-SWA) the routing inputs and outputs.
 struct StepArgs {
@@ -95,6 +108,8 @@ hipError_t launch_srswa_decode(int dtype, int head_dim, const DecodeArgs& a, hip
 hipError_t launch_block_index(int dtype, int head_dim, const IndexArgs& a, hipStream_t s);
 hipError_t launch_block_score(int dtype, int head_dim, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_entmax_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_prefill_route(int dtype, int head_dim, const PrefillArgs& a, hipStream_t s);
+int prefill_queries_per_wg(int nb_cap);
 hipError_t launch_srswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
 hipError_t launch_rswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
 

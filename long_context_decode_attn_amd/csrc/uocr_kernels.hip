@@ -1424,6 +1424,171 @@ __global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// uocr_prefill_route: the routing of a prefill chunk.  A workgroup takes qt
+// consecutive queries of one unit:
+//   1. q_idx = P^T q of each query (fp64, one thread per (query, index dim));
+//   2. the scores of every block visible to the tile's last query against the
+//      tile's queries (fp64, rounded once, into LDS); each thread holds one
+//      block key in registers and runs it against every query that may see it;
+//   3. each wave routes its queries (w, w + 8, ...) on the one-wave path.
+// A query that path cannot take (more than 1024 visible blocks, or more than
+// 64 candidates) is marked in sel_idx[0] and routed by k_prefill_fallback,
+// which runs next in the same stream with the whole workgroup per query (its
+// register needs would halve this kernel's occupancy).  Query i of the chunk
+// sits at position q_pos[b] + i and sees the blocks all of whose prefix tokens
+// come before it.
+// ---------------------------------------------------------------------------
+constexpr int kPrefillThreads = 512;
+constexpr int kPrefillScores = 8192;  // LDS score slots: qt x nb_cap
+constexpr int kPrefillMaxQ = 16;
+constexpr int32_t kDeferred = INT32_MIN;
+
+struct PrefillSmem {
+  float scores[kPrefillScores];
+  alignas(16) double qidx[kPrefillMaxQ][kIdxDim];
+  PairBuf pb[kPrefillThreads / 64];  // one per wave
+};
+
+// Query i of the tile starting at chunk query q0: position and visible blocks.
+struct PrefillTile {
+  int unit, q0, nq, m, nb_all;
+  long long pos0;
+  __device__ PrefillTile(const PrefillArgs& a) {
+    const int tiles = (a.tq + a.qt - 1) / a.qt;
+    unit = blockIdx.x / tiles;
+    q0 = (blockIdx.x - unit * tiles) * a.qt;
+    nq = min(a.qt, a.tq - q0);
+    const int b = unit / a.heads;
+    m = min(max(a.prefix_len[b], 0), a.prefix_cap);
+    nb_all = min((m + kBlock - 1) / kBlock, a.nb_cap);
+    pos0 = (long long)a.q_pos[b] + q0;
+  }
+  __device__ int visible(int qi) const {  // non-decreasing in qi
+    const long long t = pos0 + qi;
+    return t >= m ? nb_all : (int)(max(t, 0ll) / kBlock);
+  }
+};
+
+// q_idx of query qi of the tile, index dim i (fp64).
+template <int DT, int D>
+__device__ __forceinline__ double prefill_qidx(const PrefillArgs& a, const PrefillTile& t, int qi, int i) {
+  using G = Geo<DT, D>;
+  const char* qrow = static_cast<const char*>(a.q) + ((size_t)t.unit * a.tq + t.q0 + qi) * G::ROWB;
+  double acc = 0.0;
+  for (int dd = 0; dd < D; ++dd) {
+    float qd;
+    if constexpr (DT == 0)
+      qd = reinterpret_cast<const float*>(qrow)[dd];
+    else
+      qd = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[dd] << 16);
+    acc += (double)a.proj[dd * kIdxDim + i] * (double)qd;
+  }
+  return acc;
+}
+
+// Score of block key kv (fp64 copy) against q_idx (LDS), rounded once.
+__device__ __forceinline__ float prefill_score(const double* qidx, const double (&kv)[kIdxDim]) {
+  const double2* qv = reinterpret_cast<const double2*>(qidx);
+  double sc = 0.0;
+#pragma unroll
+  for (int c = 0; c < kIdxDim / 2; ++c) {
+    const double2 x = qv[c];
+    sc += x.x * kv[2 * c] + x.y * kv[2 * c + 1];
+  }
+  return (float)sc;
+}
+
+__device__ __forceinline__ void load_key(const float* K, int j, double (&kv)[kIdxDim]) {
+  const float4* kr = reinterpret_cast<const float4*>(K + (size_t)j * kIdxDim);
+#pragma unroll
+  for (int u = 0; u < kIdxDim / 4; ++u) {
+    const float4 x = kr[u];
+    kv[4 * u] = x.x;
+    kv[4 * u + 1] = x.y;
+    kv[4 * u + 2] = x.z;
+    kv[4 * u + 3] = x.w;
+  }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArgs a) {
+  constexpr int W = kPrefillThreads / 64;
+  __shared__ PrefillSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const PrefillTile t(a);
+  const int nbmax = t.visible(t.nq - 1);
+
+  // 1. q_idx
+  {
+    const int qi = tid / kIdxDim, i = tid % kIdxDim;
+    if (qi < t.nq) sm.qidx[qi][i] = prefill_qidx<DT, D>(a, t, qi, i);
+  }
+  __syncthreads();
+
+  // 2. scores
+  const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
+  for (int j = tid; j < nbmax; j += kPrefillThreads) {
+    double kv[kIdxDim];
+    load_key(K, j, kv);
+    for (int qi = 0; qi < t.nq; ++qi)
+      if (j < t.visible(qi)) sm.scores[qi * a.nb_cap + j] = prefill_score(sm.qidx[qi], kv);
+  }
+  __syncthreads();
+
+  // 3. one-wave routing
+  for (int qi = wave; qi < t.nq; qi += W) {
+    const int nbq = t.visible(qi);
+    const int kk = min(a.topk, nbq);
+    const size_t o = ((size_t)t.unit * a.tq + t.q0 + qi) * a.topk;
+    for (int i = kk + lane; i < a.topk; i += 64) {
+      a.sel_idx[o + i] = -1;
+      if (a.sel_prob) a.sel_prob[o + i] = 0.f;
+      a.sel_bias[o + i] = -INFINITY;
+    }
+    if (kk == 0) continue;
+    const float* sq = sm.scores + qi * a.nb_cap;
+    int32_t* oi = a.sel_idx + o;
+    float* op = a.sel_prob ? a.sel_prob + o : nullptr;
+    float* ob = a.sel_bias + o;
+    bool ok = false;
+    if (nbq <= 64) ok = wave_route<1>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    else if (nbq <= 128) ok = wave_route<2>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    else if (nbq <= 256) ok = wave_route<4>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    else if (nbq <= 512) ok = wave_route<8>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    else if (nbq <= 64 * kWaveBlocks) ok = wave_route<16>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    if (!ok && lane == 0) oi[0] = kDeferred;
+  }
+}
+
+// The queries k_prefill_route left marked: scores again (one query at a time)
+// and the whole-workgroup routing.  Same grid as k_prefill_route.
+template <int DT, int D>
+__global__ __launch_bounds__(kPrefillThreads) void k_prefill_fallback(PrefillArgs a) {
+  __shared__ TopkSmem<kPrefillThreads> tsm;
+  __shared__ float scores[kMaxBlocks];
+  __shared__ alignas(16) double qidx[kIdxDim];
+  const int tid = threadIdx.x;
+  const PrefillTile t(a);
+  const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
+  for (int qi = 0; qi < t.nq; ++qi) {
+    const size_t o = ((size_t)t.unit * a.tq + t.q0 + qi) * a.topk;
+    if (a.sel_idx[o] != kDeferred) continue;  // uniform: every thread reads the same word
+    __syncthreads();                          // the previous query is done with the LDS
+    if (tid < kIdxDim) qidx[tid] = prefill_qidx<DT, D>(a, t, qi, tid);
+    __syncthreads();
+    const int nbq = t.visible(qi);
+    for (int j = tid; j < nbq; j += kPrefillThreads) {
+      double kv[kIdxDim];
+      load_key(K, j, kv);
+      scores[j] = prefill_score(qidx, kv);
+    }
+    __syncthreads();
+    entmax_topk_block<kPrefillThreads>(scores, nbq, a.topk, a.sel_idx + o, a.sel_prob ? a.sel_prob + o : nullptr,
+                                       a.sel_bias + o, nullptr, nullptr, tsm);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fused steps: append + (route +) decode in one launch
 // ---------------------------------------------------------------------------
 // uocr_srswa_step: one workgroup of NT threads per unit runs the whole step.
@@ -1727,6 +1892,22 @@ hipError_t launch_block_score(int dtype, int head_dim, const ScoreArgs& a, hipSt
 
 hipError_t launch_entmax_topk(const TopkArgs& a, hipStream_t s) {
   k_entmax_topk<<<dim3(a.units), dim3(kTopkThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+int prefill_queries_per_wg(int nb_cap) {
+  const int q = nb_cap > 0 ? kPrefillScores / nb_cap : kPrefillMaxQ;
+  return q < kPrefillMaxQ ? q : kPrefillMaxQ;
+}
+
+hipError_t launch_prefill_route(int dtype, int head_dim, const PrefillArgs& a, hipStream_t s) {
+  if (a.tq == 0 || a.units == 0) return hipSuccess;
+  const long long tiles = (a.tq + a.qt - 1) / a.qt;
+  const dim3 grid((unsigned)(a.units * tiles));
+  UOCR_DISPATCH(k_prefill_route, grid, dim3(kPrefillThreads), a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  UOCR_DISPATCH(k_prefill_fallback, grid, dim3(kPrefillThreads), a);
   return hipGetLastError();
 }
 

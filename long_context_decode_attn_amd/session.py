@@ -87,6 +87,17 @@ class DecodeSession:
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
         U.uocr_ring_append(self.shape, self.k_ring, self.v_ring, k_new, v_new, self.t_gen)
 
+    def prefill_route(self, q: torch.Tensor, q_pos: torch.Tensor):
+        """Routing of a prefill chunk q [B][H][tq][D] whose query 0 sits at
+        position q_pos[b] (int32 [B]); returns (idx, prob, bias) [B][H][tq][k]."""
+        B, H, tq, k = q.shape[0], q.shape[1], q.shape[2], self.route.topk
+        idx = torch.empty((B, H, tq, k), dtype=torch.int32, device=q.device)
+        prob = torch.empty((B, H, tq, k), dtype=torch.float32, device=q.device)
+        bias = torch.empty((B, H, tq, k), dtype=torch.float32, device=q.device)
+        U.uocr_prefill_route(self.shape, self.route, q, q_pos, self.proj, self.kbar, self.prefix_len,
+                             idx, prob, bias)
+        return idx, prob, bias
+
     def score(self, q: torch.Tensor) -> None:
         U.uocr_block_score(self.shape, self.route, q, self.proj, self.kbar, self.prefix_len, self.scores)
 

@@ -29,7 +29,7 @@ WINDOW = 128
 
 # Independent random streams; the value is the first element of the
 # SeedSequence spawn key, the second is the sequence index (or the step).
-_S_PROJ, _S_QSTAR, _S_KP, _S_VP, _S_RING, _S_STEP, _S_PLANT, _S_Q, _S_MISC = range(9)
+_S_PROJ, _S_QSTAR, _S_KP, _S_VP, _S_RING, _S_STEP, _S_PLANT, _S_Q, _S_MISC, _S_PREFILL = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -234,6 +234,23 @@ def step_query(w: Workload, step: int) -> np.ndarray:
         q = np.stack([fixed_query_f32(w, b) for b in range(w.batch)]).astype(np.float32)
         return store(q, w.dtype)
     return store(normal32(w.seed, (w.batch, w.heads, w.head_dim), _S_Q, step), w.dtype)
+
+
+def prefill_queries(w: Workload, tq: int, chunk: int = 0) -> np.ndarray:
+    """Queries of a prefill chunk, storage array [B][H][tq][D].  Query i of a
+    sequence is, by i mod 4: the planted q* plus N(0, 1/4) noise (routes to
+    the planted blocks), plain N(0, 1), q* itself, or N(0, 1) scaled by 1e-3
+    (nearly flat scores: many blocks tie for the entmax support).  Without
+    planted queries every kind is N(0, 1), scaled as above."""
+    z = normal32(w.seed, (w.batch, w.heads, tq, w.head_dim), _S_PREFILL, chunk)
+    kind = np.arange(tq) % 4
+    q = z.copy()
+    if w.fixed_query:
+        qs = np.stack([fixed_query_f32(w, b) for b in range(w.batch)]).astype(np.float32)[:, :, None, :]
+        q = np.where((kind == 0)[None, None, :, None], qs + np.float32(0.5) * z, q)
+        q = np.where((kind == 2)[None, None, :, None], np.broadcast_to(qs, q.shape), q)
+    q = np.where((kind == 3)[None, None, :, None], z * np.float32(1e-3), q)
+    return store(q.astype(np.float32), w.dtype)
 
 
 def step_inputs(w: Workload, step: int):

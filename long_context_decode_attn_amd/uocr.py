@@ -115,6 +115,7 @@ def load_library():
         "uocr_block_index_build": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P]),
         "uocr_block_score": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P]),
         "uocr_entmax15_topk": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P]),
+        "uocr_prefill_route": (ctypes.c_int, [SP, RP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
         "uocr_srswa_splits": (_I32, [SP, RP, _I32]),
         "uocr_srswa_decode": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
         "uocr_rswa_step": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P]),
@@ -134,6 +135,7 @@ def load_library():
 
 EXPORTED = ("uocr_ring_append", "uocr_rswa_splits", "uocr_rswa_workspace_bytes",
             "uocr_rswa_decode", "uocr_block_index_build", "uocr_block_score", "uocr_entmax15_topk",
+            "uocr_prefill_route",
             "uocr_srswa_splits", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
             "uocr_status_string", "uocr_last_error", "uocr_version")
 
@@ -259,6 +261,24 @@ def uocr_entmax15_topk(shape: Shape, route: Route, scores, prefix_len, sel_idx, 
     _check(sel_bias, "sel_bias", torch.float32, (B, H, k))
     _call("uocr_entmax15_topk", ctypes.byref(shape.c()), ctypes.byref(route.c()), _ptr(scores), _ptr(prefix_len),
           _ptr(sel_idx), _ptr(sel_prob), _ptr(sel_bias), _stream(stream))
+
+
+def uocr_prefill_route(shape: Shape, route: Route, q, q_pos, proj, kbar, prefix_len, sel_idx, sel_prob, sel_bias,
+                       stream=None) -> None:
+    """q [B][H][tq][D]; q_pos [B] int32; outputs [B][H][tq][topk]."""
+    B, H, D, k = shape.batch, shape.heads, shape.head_dim, route.topk
+    tq = int(q.shape[2]) if q.dim() == 4 else -1
+    _check(q, "q", shape.torch_dtype, (B, H, tq, D))
+    _check(q_pos, "q_pos", torch.int32, (B,))
+    _check(proj, "proj", torch.float32, (D, 32))
+    _check(kbar, "kbar", torch.float32, (B, H, shape.nb_cap, 32), optional=shape.nb_cap == 0)
+    _check(prefix_len, "prefix_len", torch.int32, (B,))
+    _check(sel_idx, "sel_idx", torch.int32, (B, H, tq, k))
+    _check(sel_prob, "sel_prob", torch.float32, (B, H, tq, k), optional=True)
+    _check(sel_bias, "sel_bias", torch.float32, (B, H, tq, k))
+    _call("uocr_prefill_route", ctypes.byref(shape.c()), ctypes.byref(route.c()), _ptr(q), tq, _ptr(q_pos),
+          _ptr(proj), _ptr(kbar), _ptr(prefix_len), _ptr(sel_idx), _ptr(sel_prob), _ptr(sel_bias),
+          _stream(stream))
 
 
 def uocr_srswa_decode(shape: Shape, route: Route, q, k_prefix, v_prefix, prefix_len, sel_idx, sel_bias,

@@ -102,6 +102,23 @@ def test_route_validation():
     assert lib.uocr_block_index_build(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, None, FAKE, None) == -1
 
 
+def test_prefill_route_validation():
+    U, lib = _lib()
+    sh = _shape(U)
+    r = U._Route(32, 32, 16)
+    call = lambda tq, q=FAKE, qpos=FAKE, idx=FAKE: lib.uocr_prefill_route(
+        ctypes.byref(sh), ctypes.byref(r), q, tq, qpos, FAKE, FAKE, FAKE, idx, None, FAKE, None)
+    assert call(-1) == -2
+    assert call((1 << 20) + 1) == -2
+    assert call(0, q=None, qpos=None, idx=None) == 0      # nothing to do, nothing launched
+    assert call(8, q=None) == -1
+    assert call(8, qpos=None) == -1
+    assert call(8, q=ODD) == -5
+    big = _shape(U, batch=4096, heads=64)
+    assert lib.uocr_prefill_route(ctypes.byref(big), ctypes.byref(r), FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None, FAKE, None) == -2    # outputs beyond 2^31 entries
+
+
 def test_split_geometry():
     U, lib = _lib()
     for B, H, m in [(64, 10, 2592), (512, 10, 288), (1, 2, 528), (32, 10, 10240), (8, 10, 32000), (1, 1, 0)]:
