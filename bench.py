@@ -64,6 +64,9 @@ def parse():
                     help="fused: one uocr_*_step launch per step; separate: one launch per row")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-route", type=int, default=0, metavar="TQ",
+                    help="instead of the decode step, time uocr_prefill_route on a chunk of TQ queries per "
+                         "(sequence, head) (the sparse workload's last TQ prefix positions)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (known bytes) so that a "
                          "counter profile of this run can scale FETCH_SIZE / WRITE_SIZE")
@@ -164,12 +167,108 @@ def cpu_baseline(w, budget_s: float):
 
 
 # ----------------------------------------------------------------------------
+# prefill-side routing (a separate measurement; the decode step is the default)
+# ----------------------------------------------------------------------------
+FP64_PEAK_TFLOPS = 78.6
+
+
+def prefill_cpu_baseline(w, tq, q_pos, budget_s):
+    """The oracle's prefill_route_unit on whole units of the same chunk, one
+    at a time, until the budget is spent; returns queries/s."""
+    from threadpoolctl import threadpool_limits
+
+    from long_context_decode_attn_amd import synth as S
+    from oracle import uocr_oracle as O
+    P = S.projection(w).astype(np.float64)
+    qd = S.widen(S.prefill_queries(w, tq), w.dtype)[:, :, :tq]
+    Kp, _ = S.prefix_kv_seq(w, 0)
+    done, units, spent = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while spent < budget_s:
+            h = units % w.heads
+            kb = O.block_index(S.widen(Kp[h], w.dtype), w.prefix_len, P)   # one-time per unit, not timed
+            t1 = time.perf_counter()
+            O.prefill_route_unit(qd[0, h], q_pos, P, kb, w.prefix_len, w.topk)
+            spent += time.perf_counter() - t1
+            done += len(qd[0, h])
+            units += 1
+    dt = spent
+    return {"value": done / dt, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} queries ({units} units x {tq}) of {w.name}, float64 numpy, 1 thread"}
+
+
+def prefill_main(args):
+    import torch
+
+    from long_context_decode_attn_amd import synth as S
+    from long_context_decode_attn_amd import uocr as U
+    from long_context_decode_attn_amd.session import DecodeSession, to_device
+
+    U.load_library()
+    w = S.WORKLOADS[args.workload]
+    assert w.sparse, "prefill routing needs a sparse workload"
+    tq = args.prefill_route
+    q_pos = max(w.prefix_len - tq, 0)
+    sessions = [DecodeSession(w)]
+    sessions += [sessions[0].clone() for _ in range(3)]
+    for s in sessions:
+        s.build_index()
+    q = to_device(S.prefill_queries(w, tq), w.dtype)
+    pos = torch.full((w.batch,), q_pos, dtype=torch.int32, device="cuda")
+    outs = [tuple(torch.empty((w.batch, w.heads, tq, w.topk), dtype=dt, device="cuda")
+                  for dt in (torch.int32, torch.float32, torch.float32)) for _ in sessions]
+
+    def run(i):
+        s, (idx, prob, bias) = sessions[i % len(sessions)], outs[i % len(sessions)]
+        U.uocr_prefill_route(s.shape, s.route, q, pos, s.proj, s.kbar, s.prefix_len, idx, prob, bias)
+
+    for i in range(max(args.warmup // 20, 3)):
+        run(i)
+    torch.cuda.synchronize()
+    K = max(args.steps // 100, 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    queries = w.units * tq
+    nb = w.n_blocks
+    visible = sum(min(nb, (q_pos + i) // w.block) if q_pos + i < w.prefix_len else nb for i in range(tq))
+    flops = w.units * (2.0 * w.idx_dim * visible + 2.0 * w.head_dim * w.idx_dim * tq)
+    achieved = flops / (ms * 1e-3) / 1e12
+    hbm = w.units * (tq * w.head_dim * w.elem_bytes + nb * w.idx_dim * 4 + tq * w.topk * 12)
+    idx = outs[(K - 1) % len(sessions)][0]
+    result = {
+        "metric": "prefill routing queries/s (batch x heads x chunk tokens)", "value": round(queries / (ms * 1e-3), 1),
+        "unit": "queries/s", "n_gpus": 1, "steps": K, "warmup": max(args.warmup // 20, 3),
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": w.name + f"-prefill-chunk{tq}", "batch": w.batch, "heads": w.heads,
+                   "prefix_tokens": w.prefix_len, "blocks": nb, "chunk_queries": tq, "chunk_start": q_pos,
+                   "topk": w.topk, "sessions_cycled": len(sessions)},
+        "roofline": {"kernel": "uocr_prefill_route", "bound": "alu", "achieved": round(achieved, 2),
+                     "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP64_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "flops_per_launch": flops, "hbm_bytes_per_launch": hbm,
+        "hbm_gbs": round(hbm / (ms * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(w, min(tq, 256), q_pos, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+# ----------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode path has no "
               f"cross-GPU step; see DESIGN.md for how it would shard.", file=sys.stderr)
         sys.exit(2)
+
+    if args.prefill_route:
+        return prefill_main(args)
 
     import torch
 

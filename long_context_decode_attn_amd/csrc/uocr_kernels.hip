@@ -902,9 +902,25 @@ struct NoOverlap {
   __device__ void operator()() const {}
 };
 
+// Sum of a double over the 64 lanes, the same value in every lane.
+__device__ __forceinline__ double wave_sum_d(double x) {
+  x = group_sum<16>(x);
+  return readlane_d(x, 0) + readlane_d(x, 16) + readlane_d(x, 32) + readlane_d(x, 48);
+}
+
 // One-wave routing for nb <= 64 * NS blocks (see entmax_topk_block).  Returns
-// false, having written nothing, when the candidate set exceeds 64 blocks.
-template <int NS>
+// false, having written nothing, when it cannot finish: more than 64 blocks
+// tie around the k-th score, or (unless WIDE) the entmax candidates (d <= 2)
+// alone are more than 64.
+//
+// WIDE: a support too large for per-candidate statistics is handled here too.
+// A then only has to hold the top kk, and the threshold comes from Newton's
+// method on f(tau) = sum_j max(0, u_j - tau)^2 = 1 (convex, decreasing: from
+// tau = u_max - 1 the iterates rise monotonically to the root), followed by
+// the closed form of the sorted algorithm on the support S = {u > tau} found,
+// accepted only if it satisfies the optimality conditions (u > tau_S on S,
+// u <= tau_S off S), which single out the exact support.
+template <int NS, bool WIDE = false>
 __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32_t* o_idx, float* o_prob,
                                            float* o_bias, int* l_idx, float* l_bias, PairBuf& pb) {
   const int lane = threadIdx.x & 63;
@@ -934,13 +950,46 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
     if (nA >= kk) break;
     T = T * 2.f;  // reaches +inf, where every finite d counts
   }
+  // Too many blocks below T for one wave: bisect T in (lo, hi) for a count in
+  // [kk, 64]; count(d < lo) < kk, except possibly at the first probe.
+  auto narrow = [&](float lo, float hi) -> bool {
+    for (int it = 0; it < 48; ++it) {
+      const float mid = it == 0 ? lo : 0.5f * (lo + hi);
+      if (it > 0 && !(mid > lo && mid < hi)) return false;
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < NS; ++e) c += dv[e] < mid ? 1 : 0;
+      c = wave_sum(c);
+      if (c >= kk && c <= 64) {
+        T = mid;
+        nA = c;
+        return true;
+      }
+      if (c > 64) {
+        if (it == 0) return false;
+        hi = mid;
+      } else {
+        lo = mid;
+      }
+    }
+    return false;
+  };
+  // T never below the least float above 2 keeps every d <= 2 (every entmax
+  // candidate) in A
+  bool wide = false;
+  if (nA > 64) {
+    const float hi = T;
+    if (!narrow(fmaxf(0.5f * T, __uint_as_float(0x40000001u)), hi)) {
+      if constexpr (WIDE) wide = narrow(0.f, hi);
+    }
+  }
   if (nA <= 64) {
     // ordered compaction of A (and of the entmax candidates) by ballots
     int base = 0, cbase = 0;
 #pragma unroll
     for (int e = 0; e < NS; ++e) {
       const bool in = dv[e] < T;
-      const bool cd = ((double)sv[e] - dmax) * 0.5 > -1.0;
+      const bool cd = !wide && ((double)sv[e] - dmax) * 0.5 > -1.0;
       const uint64_t m = __ballot(in);
       const uint64_t mc = __ballot(cd);
       const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -968,7 +1017,6 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
     const float si = mine ? pb.val[lane] : -INFINITY;
     const int ii = mine ? pb.idx[lane] : 0x7fffffff;
     const double vi = ((double)si - dmax) * 0.5;
-    const bool cand = mine && vi > -1.0;
     const float4* val4 = reinterpret_cast<const float4*>(pb.val);
     const int4* idx4 = reinterpret_cast<const int4*>(pb.idx);
     int rank = 0;
@@ -979,33 +1027,82 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
       rank += (sk.x > si || (sk.x == si && ik.x < ii)) + (sk.y > si || (sk.y == si && ik.y < ii)) +
               (sk.z > si || (sk.z == si && ik.z < ii)) + (sk.w > si || (sk.w == si && ik.w < ii));
     }
-    const float4* cv4 = reinterpret_cast<const float4*>(pb.rank);
-    int r = 0;
-    double s1 = 0.0, s2 = 0.0;
-    for (int k4 = 0; k4 < nC4 / 4; ++k4) {
-      const float4 c4 = cv4[k4];
-      const float ck[4] = {c4.x, c4.y, c4.z, c4.w};
+    double tau;
+    if (!wide) {
+      const bool cand = mine && vi > -1.0;
+      const float4* cv4 = reinterpret_cast<const float4*>(pb.rank);
+      int r = 0;
+      double s1 = 0.0, s2 = 0.0;
+      for (int k4 = 0; k4 < nC4 / 4; ++k4) {
+        const float4 c4 = cv4[k4];
+        const float ck[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (ck[k] >= si) {
-          const double vk = ((double)ck[k] - dmax) * 0.5;
-          ++r;
-          s1 += vk;
-          s2 += vk * vk;
+        for (int k = 0; k < 4; ++k) {
+          if (ck[k] >= si) {
+            const double vk = ((double)ck[k] - dmax) * 0.5;
+            ++r;
+            s1 += vk;
+            s2 += vk * vk;
+          }
         }
       }
+      int rr = 0;
+      double tl = 0.0;
+      if (cand) {
+        const double mu = s1 / r;
+        const double ss = s2 - s1 * mu;
+        tl = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
+        rr = tl <= vi ? r : 0;
+      }
+      const int rstar = wave_max(rr);
+      const uint64_t win = __ballot(rr == rstar && rr > 0);
+      tau = readlane_d(tl, __ffsll((unsigned long long)win) - 1);
+    } else {
+      // u' = (s - smax) / 2 in [-inf, 0]; the root lies in [-1, 0)
+      double up[NS];
+#pragma unroll
+      for (int e = 0; e < NS; ++e) up[e] = ((double)sv[e] - dmax) * 0.5;
+      double t = -1.0;
+      for (int it = 0; it < 64; ++it) {
+        double F = 0.0, G = 0.0;
+#pragma unroll
+        for (int e = 0; e < NS; ++e) {
+          const double x = up[e] - t;
+          if (x > 0.0) {
+            F += x * x;
+            G += x;
+          }
+        }
+        F = wave_sum_d(F);
+        G = wave_sum_d(G);
+        const double step = (F - 1.0) / (2.0 * G);
+        if (!(step > 0.0) || t + step == t) break;
+        t += step;
+      }
+      int r = 0;
+      double s1 = 0.0;
+#pragma unroll
+      for (int e = 0; e < NS; ++e)
+        if (up[e] > t) {
+          ++r;
+          s1 += up[e];
+        }
+      r = wave_sum(r);
+      const double mu = wave_sum_d(s1) / r;
+      double ss = 0.0;
+#pragma unroll
+      for (int e = 0; e < NS; ++e)
+        if (up[e] > t) ss += (up[e] - mu) * (up[e] - mu);
+      ss = wave_sum_d(ss);
+      tau = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
+      bool bad = false;
+#pragma unroll
+      for (int e = 0; e < NS; ++e) bad |= (up[e] > t) ? !(up[e] > tau) : (up[e] > tau);
+      if (__ballot(bad) != 0) {
+        __builtin_amdgcn_s_setprio(0);
+        return false;
+      }
     }
-    int rr = 0;
-    double tl = 0.0;
-    if (cand) {
-      const double mu = s1 / r;
-      const double ss = s2 - s1 * mu;
-      tl = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
-      rr = tl <= vi ? r : 0;
-    }
-    const int rstar = wave_max(rr);
-    const uint64_t win = __ballot(rr == rstar && rr > 0);
-    const double tau = readlane_d(tl, __ffsll((unsigned long long)win) - 1);
     const bool sel = mine && rank < kk;
     const uint64_t sm_ = __ballot(sel);
     if (sel) {
@@ -1059,8 +1156,9 @@ __device__ __forceinline__ void entmax_topk_block(const float* s, int nb, int to
   // l, l + 64, l + 128, ... (slot e holds block l + 64 e), so index order is
   // (slot, lane) order and an ordered compaction needs only ballots.  With
   // d = smax - s in fp32 (monotone in s), the set A = {d < T}, T = 4, 8, 16,
-  // ... until it holds kk blocks, contains the top kk (ties of the kk-th
-  // included) and the entmax support (exact d < 2 gives fp32 d <= 2 < 4).  A
+  // ... until it holds kk blocks (then bisected, never below the least float
+  // above 2, while it holds more than 64), contains the top kk (ties of the
+  // kk-th included) and the entmax support (exact d < 2 gives fp32 d <= 2).  A
   // is compacted in index order into LDS; each lane takes one block of A and
   // counts, over broadcast LDS reads of A, the blocks ranked before it and
   // (for an entmax candidate) the prefix statistics of the sorted order at the
@@ -1551,40 +1649,71 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
     float* op = a.sel_prob ? a.sel_prob + o : nullptr;
     float* ob = a.sel_bias + o;
     bool ok = false;
-    if (nbq <= 64) ok = wave_route<1>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    else if (nbq <= 128) ok = wave_route<2>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    else if (nbq <= 256) ok = wave_route<4>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    else if (nbq <= 512) ok = wave_route<8>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    else if (nbq <= 64 * kWaveBlocks) ok = wave_route<16>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    if (nbq <= 64) ok = wave_route<1, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    else if (nbq <= 128) ok = wave_route<2, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    else if (nbq <= 256) ok = wave_route<4, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    else if (nbq <= 512) ok = wave_route<8, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+    else if (nbq <= 64 * kWaveBlocks) ok = wave_route<16, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
     if (!ok && lane == 0) oi[0] = kDeferred;
   }
 }
 
 // The queries k_prefill_route left marked: scores again (one query at a time)
-// and the whole-workgroup routing.  Same grid as k_prefill_route.
+// and the whole-workgroup routing.  The workgroups stride over the chunk's
+// queries 512 at a time, reading 512 markers per pass, so a chunk with no
+// marked query costs one pass of loads.
 template <int DT, int D>
 __global__ __launch_bounds__(kPrefillThreads) void k_prefill_fallback(PrefillArgs a) {
   __shared__ TopkSmem<kPrefillThreads> tsm;
   __shared__ float scores[kMaxBlocks];
   __shared__ alignas(16) double qidx[kIdxDim];
+  __shared__ int list[kPrefillThreads];
+  __shared__ int n_list;
   const int tid = threadIdx.x;
-  const PrefillTile t(a);
-  const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
-  for (int qi = 0; qi < t.nq; ++qi) {
-    const size_t o = ((size_t)t.unit * a.tq + t.q0 + qi) * a.topk;
-    if (a.sel_idx[o] != kDeferred) continue;  // uniform: every thread reads the same word
-    __syncthreads();                          // the previous query is done with the LDS
-    if (tid < kIdxDim) qidx[tid] = prefill_qidx<DT, D>(a, t, qi, tid);
+  const long long total = (long long)a.units * a.tq;
+  for (long long base = (long long)blockIdx.x * kPrefillThreads; base < total;
+       base += (long long)gridDim.x * kPrefillThreads) {
+    if (tid == 0) n_list = 0;
     __syncthreads();
-    const int nbq = t.visible(qi);
-    for (int j = tid; j < nbq; j += kPrefillThreads) {
-      double kv[kIdxDim];
-      load_key(K, j, kv);
-      scores[j] = prefill_score(qidx, kv);
+    const long long g = base + tid;
+    if (g < total && a.sel_idx[g * a.topk] == kDeferred) list[atomicAdd(&n_list, 1)] = tid;
+    __syncthreads();
+    const int nl = n_list;
+    for (int l = 0; l < nl; ++l) {
+      const long long gq = base + list[l];
+      const int unit = (int)(gq / a.tq), i = (int)(gq - (long long)unit * a.tq);
+      const int b = unit / a.heads;
+      const int m = min(max(a.prefix_len[b], 0), a.prefix_cap);
+      const int nb_all = min((m + kBlock - 1) / kBlock, a.nb_cap);
+      const long long t = (long long)a.q_pos[b] + i;
+      const int nbq = t >= m ? nb_all : (int)(max(t, 0ll) / kBlock);
+      if (tid < kIdxDim) {
+        using G = Geo<DT, D>;
+        const char* qrow = static_cast<const char*>(a.q) + (size_t)gq * G::ROWB;
+        double acc = 0.0;
+        for (int dd = 0; dd < D; ++dd) {
+          float qd;
+          if constexpr (DT == 0)
+            qd = reinterpret_cast<const float*>(qrow)[dd];
+          else
+            qd = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[dd] << 16);
+          acc += (double)a.proj[dd * kIdxDim + tid] * (double)qd;
+        }
+        qidx[tid] = acc;
+      }
+      __syncthreads();
+      const float* K = a.kbar + (size_t)unit * a.nb_cap * kIdxDim;
+      for (int j = tid; j < nbq; j += kPrefillThreads) {
+        double kv[kIdxDim];
+        load_key(K, j, kv);
+        scores[j] = prefill_score(qidx, kv);
+      }
+      __syncthreads();
+      const size_t o = (size_t)gq * a.topk;
+      entmax_topk_block<kPrefillThreads>(scores, nbq, a.topk, a.sel_idx + o, a.sel_prob ? a.sel_prob + o : nullptr,
+                                         a.sel_bias + o, nullptr, nullptr, tsm);
+      __syncthreads();
     }
-    __syncthreads();
-    entmax_topk_block<kPrefillThreads>(scores, nbq, a.topk, a.sel_idx + o, a.sel_prob ? a.sel_prob + o : nullptr,
-                                       a.sel_bias + o, nullptr, nullptr, tsm);
   }
 }
 
@@ -1907,7 +2036,9 @@ hipError_t launch_prefill_route(int dtype, int head_dim, const PrefillArgs& a, h
   UOCR_DISPATCH(k_prefill_route, grid, dim3(kPrefillThreads), a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  UOCR_DISPATCH(k_prefill_fallback, grid, dim3(kPrefillThreads), a);
+  long long passes = ((long long)a.units * a.tq + kPrefillThreads - 1) / kPrefillThreads;
+  if (passes > 1024) passes = 1024;
+  UOCR_DISPATCH(k_prefill_fallback, dim3((unsigned)passes), dim3(kPrefillThreads), a);
   return hipGetLastError();
 }
 

@@ -96,3 +96,13 @@ def test_prefill_route_full_size_125_pages_sampled():
     w = S.WORKLOADS["srswa-125p-b8"]
     say("prefill route full size")
     _run(w, 64, [w.prefix_len - 48] * w.batch, units=[(0, 0), (1, 3), (3, 9), (5, 5), (7, 1), (7, 8)])
+
+
+def test_prefill_route_wide_entmax_support():
+    """200 blocks and near-flat scores for a quarter of the queries: the
+    entmax support holds far more than 64 blocks, so those queries take the
+    wide path (Newton on the threshold, closed form on the support found)."""
+    need_gpu()
+    w = _small(pages=25, planted=10)
+    say("prefill route wide support")
+    _run(w, 64, [w.prefix_len - 16, w.prefix_len - 40])
