@@ -1537,7 +1537,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
 // come before it.
 // ---------------------------------------------------------------------------
 constexpr int kPrefillThreads = 512;
-constexpr int kPrefillScores = 8192;  // LDS score slots: qt x nb_cap
+constexpr int kPrefillScores = 12288;  // LDS score slots: qt x nb_cap
 constexpr int kPrefillMaxQ = 16;
 constexpr int32_t kDeferred = INT32_MIN;
 
@@ -1566,23 +1566,6 @@ struct PrefillTile {
     return t >= m ? nb_all : (int)(max(t, 0ll) / kBlock);
   }
 };
-
-// q_idx of query qi of the tile, index dim i (fp64).
-template <int DT, int D>
-__device__ __forceinline__ double prefill_qidx(const PrefillArgs& a, const PrefillTile& t, int qi, int i) {
-  using G = Geo<DT, D>;
-  const char* qrow = static_cast<const char*>(a.q) + ((size_t)t.unit * a.tq + t.q0 + qi) * G::ROWB;
-  double acc = 0.0;
-  for (int dd = 0; dd < D; ++dd) {
-    float qd;
-    if constexpr (DT == 0)
-      qd = reinterpret_cast<const float*>(qrow)[dd];
-    else
-      qd = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[dd] << 16);
-    acc += (double)a.proj[dd * kIdxDim + i] * (double)qd;
-  }
-  return acc;
-}
 
 // Score of block key kv (fp64 copy) against q_idx (LDS), rounded once.
 __device__ __forceinline__ float prefill_score(const double* qidx, const double (&kv)[kIdxDim]) {
@@ -1616,20 +1599,67 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
   const PrefillTile t(a);
   const int nbmax = t.visible(t.nq - 1);
 
-  // 1. q_idx
+  // 1. q_idx: P and the tile's queries are staged in the (not yet used)
+  //    score buffer with coalesced loads, then one thread per (query, dim)
   {
+    float* Ps = sm.scores;                 // [D][32]
+    float* Qs = sm.scores + D * kIdxDim;   // [nq][D]
+    for (int e = tid; e < D * kIdxDim; e += kPrefillThreads) Ps[e] = a.proj[e];
+    const char* q0 = static_cast<const char*>(a.q) + ((size_t)t.unit * a.tq + t.q0) * Geo<DT, D>::ROWB;
+    for (int e = tid; e < t.nq * D; e += kPrefillThreads) {
+      if constexpr (DT == 0)
+        Qs[e] = reinterpret_cast<const float*>(q0)[e];
+      else
+        Qs[e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(q0)[e] << 16);
+    }
+    __syncthreads();
     const int qi = tid / kIdxDim, i = tid % kIdxDim;
-    if (qi < t.nq) sm.qidx[qi][i] = prefill_qidx<DT, D>(a, t, qi, i);
+    if (qi < t.nq) {
+      double acc = 0.0;
+      for (int dd = 0; dd < D; ++dd) acc += (double)Ps[dd * kIdxDim + i] * (double)Qs[qi * D + dd];
+      sm.qidx[qi][i] = acc;
+    }
   }
   __syncthreads();
 
-  // 2. scores
-  const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
-  for (int j = tid; j < nbmax; j += kPrefillThreads) {
-    double kv[kIdxDim];
-    load_key(K, j, kv);
-    for (int qi = 0; qi < t.nq; ++qi)
-      if (j < t.visible(qi)) sm.scores[qi * a.nb_cap + j] = prefill_score(sm.qidx[qi], kv);
+  // 2. scores on the matrix cores, fp64: tile (16 queries) x (16 blocks),
+  //    S = Qidx [16 x 32] . KBAR^T [32 x 16] in 8 steps of
+  //    v_mfma_f64_16x16x4f64.  Operand layout (checked on gfx950): lane l
+  //    holds A[l % 16][k] and B[k][l % 16] with k = 4 s + l / 16 at step s;
+  //    register r of the result holds S[l / 16 + 4 r][l % 16].
+  {
+    typedef double v4d __attribute__((ext_vector_type(4)));
+    const int lr = lane % 16, lk = lane / 16;
+    double af[kIdxDim / 4];
+#pragma unroll
+    for (int st = 0; st < kIdxDim / 4; ++st) af[st] = lr < t.nq ? sm.qidx[lr][4 * st + lk] : 0.0;
+    const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
+    const int ntiles = (nbmax + 15) / 16;
+    auto load_b = [&](float (&bf)[kIdxDim / 4], int tile) {  // this lane's column of a key tile
+      const int j = tile * 16 + lr;
+      const bool jok = j < nbmax;
+      const float* kr = K + (size_t)(jok ? j : 0) * kIdxDim + lk;
+#pragma unroll
+      for (int st = 0; st < kIdxDim / 4; ++st) bf[st] = jok ? kr[4 * st] : 0.f;
+    };
+    float bn[kIdxDim / 4];
+    if (wave < ntiles) load_b(bn, wave);
+    for (int tile = wave; tile < ntiles; tile += W) {
+      const int j = tile * 16 + lr;
+      float bf[kIdxDim / 4];
+#pragma unroll
+      for (int st = 0; st < kIdxDim / 4; ++st) bf[st] = bn[st];
+      if (tile + W < ntiles) load_b(bn, tile + W);  // next tile's keys in flight meanwhile
+      v4d acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int st = 0; st < kIdxDim / 4; ++st)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[st], (double)bf[st], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qq = lk + 4 * r;
+        if (qq < t.nq && j < t.visible(qq)) sm.scores[qq * a.nb_cap + j] = (float)acc[r];
+      }
+    }
   }
   __syncthreads();
 
