@@ -377,6 +377,51 @@ def prefill_route_unit(q_rows: np.ndarray, q_pos: int, proj: np.ndarray, kbar: n
 
 
 # ============================================================================
+# Windowed no-repeat n-gram ban   ([Unlimited OCR Works README mirror] SGLang
+# client example: the custom logit processor with ngram_size 35, window_size
+# 128 for one page / 1024 for several, page_token_id, eos_token_id and
+# max_page_tokens, the per-page output cap; [Unlimited OCR blog] inference
+# parameters no_repeat_ngram_size / ngram_window)
+# ============================================================================
+# Readings (the pages give the parameters only): the next token is banned
+# (logit -inf) when it would complete an n-gram equal to one lying wholly in
+# the last `window` generated tokens; the page guard, once the current page
+# has produced max_page_tokens tokens (> 0), leaves only the page marker and
+# end-of-sequence open.
+
+def ngram_banned(gen: Sequence[int], n: int, window: int) -> List[int]:
+    """Tokens the next step may not produce.  gen = the generated tokens so
+    far.  Inside the last `window` of them, every earlier n-gram whose first
+    n-1 tokens equal the last n-1 generated tokens bans its n-th token."""
+    gen = list(gen)
+    T = len(gen)
+    w = gen[max(0, T - window):]
+    if n < 1 or len(w) < n:
+        return []
+    tail = w[len(w) - (n - 1):] if n > 1 else []
+    banned = []
+    for p in range(0, len(w) - n + 1):
+        if w[p:p + n - 1] == tail:
+            banned.append(w[p + n - 1])
+    return sorted(set(banned))
+
+
+def ngram_process(logits: np.ndarray, gen: Sequence[int], n: int, window: int,
+                  page_tokens: int, max_page_tokens: int, page_token: int, eos_token: int) -> np.ndarray:
+    """The processed logits of one sequence (a copy): the page guard, then
+    the n-gram ban."""
+    out = np.array(logits, copy=True)
+    if max_page_tokens > 0 and page_tokens >= max_page_tokens:
+        keep = {page_token, eos_token}
+        for v in range(len(out)):
+            if v not in keep:
+                out[v] = NEG_INF
+    for v in ngram_banned(gen, n, window):
+        out[v] = NEG_INF
+    return out
+
+
+# ============================================================================
 # Whole routing of a batch, and the certified-gap rule for near-ties
 # ============================================================================
 def route(q, k_prefix, prefix_len, proj, k: int, block: int = 32):

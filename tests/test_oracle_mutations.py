@@ -142,3 +142,13 @@ def test_prefill_route_ignoring_chunk_position_is_caught():
     def prefill_route_unit(q, q_pos, P, kbar, m, k, block=32):
         return O.prefill_route_unit(q, 0, P, kbar, m, k, block)
     _fails(T.check_prefill_route, prefill_route_unit=prefill_route_unit)
+
+
+def test_ngram_window_counting_the_unmatched_tail_is_caught():
+    def ngram_banned(gen, n, window):
+        return O.ngram_banned(gen, n, window + 1)
+    _fails(T.check_ngram, ngram_banned=ngram_banned)
+
+
+def test_ngram_matching_one_token_short_is_caught():
+    _fails(T.check_ngram, ngram_banned=lambda gen, n, window: O.ngram_banned(gen, max(n - 1, 1), window))

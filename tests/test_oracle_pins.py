@@ -465,3 +465,49 @@ def check_prefill_route(visible_blocks=O.visible_blocks, prefill_route_unit=O.pr
 
 def test_prefill_route_causal_and_enumerated():
     check_prefill_route()
+
+
+# ----------------------------------------------------------------------------
+# windowed no-repeat n-gram ban
+# ----------------------------------------------------------------------------
+def _ngram_by_dictionary(gen, n, window):
+    """Every n-gram inside the window goes into a dictionary from its first
+    n-1 tokens to the tokens that followed them; the ban is the entry of the
+    last n-1 tokens."""
+    w = list(gen)[-window:] if window > 0 else []
+    table = {}
+    for p in range(len(w) - n + 1):
+        table.setdefault(tuple(w[p:p + n - 1]), set()).add(w[p + n - 1])
+    if len(w) < n:
+        return []
+    return sorted(table.get(tuple(w[len(w) - n + 1:]), set()))
+
+
+def check_ngram(ngram_banned=O.ngram_banned, ngram_process=O.ngram_process):
+    # worked cases
+    assert ngram_banned([5, 6, 7, 5, 6], 3, 128) == [7]          # "5 6 7 ... 5 6" bans 7
+    assert ngram_banned([5, 6, 7, 5, 6, 9, 5, 6], 3, 128) == [7, 9]
+    assert ngram_banned([5, 6, 7, 5, 6], 3, 4) == []              # 5 6 7 starts outside the window
+    assert ngram_banned([5, 6, 7, 5, 6], 3, 5) == [7]             # ... and just inside it
+    assert ngram_banned([1, 2], 3, 128) == []                     # shorter than n
+    assert ngram_banned([4, 4, 4, 4], 1, 128) == [4]              # n = 1: every token in the window
+    assert ngram_banned([3, 3, 3], 2, 128) == [3]
+    # brute force against a dictionary of n-grams, random small vocabularies
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        T = int(rng.integers(0, 60))
+        gen = rng.integers(0, int(rng.integers(1, 5)), size=T).tolist()
+        n, window = int(rng.integers(1, 7)), int(rng.integers(1, 70))
+        assert ngram_banned(gen, n, window) == _ngram_by_dictionary(gen, n, window), (gen, n, window)
+    # page guard: only the page marker and end-of-sequence stay open
+    lg = np.arange(10, dtype=np.float64)
+    out = ngram_process(lg, [1, 2, 1], 2, 128, page_tokens=20, max_page_tokens=20, page_token=7, eos_token=1)
+    assert np.isneginf(out[[0, 2, 3, 4, 5, 6, 8, 9]]).all() and out[7] == 7 and out[1] == 1
+    out = ngram_process(lg, [1, 2, 1], 2, 128, page_tokens=19, max_page_tokens=20, page_token=7, eos_token=1)
+    assert np.isneginf(out[2]) and np.isfinite(np.delete(out, 2)).all()
+    out = ngram_process(lg, [1, 2, 1], 2, 128, page_tokens=99, max_page_tokens=0, page_token=7, eos_token=1)
+    assert np.isneginf(out[2]) and np.isfinite(np.delete(out, 2)).all()   # cap <= 0 disables the guard
+
+
+def test_ngram_ban_worked_cases_and_brute_force():
+    check_ngram()
