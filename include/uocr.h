@@ -205,6 +205,33 @@ int uocr_prefill_route(const uocr_shape* shape, const uocr_route* route,
                        float* sel_prob, float* sel_bias, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * uocr_ngram_ban -- windowed no-repeat n-gram ban and per-page output cap
+ * over one decode step's logits, in place.
+ * [Unlimited OCR Works README mirror (git.zoyku.com), SGLang client example:
+ * the custom logit processor with ngram_size 35, window_size 128 (one page) /
+ * 1024 (several), page_token_id, eos_token_id and max_page_tokens, the
+ * per-page output cap; "百度 Unlimited OCR 深度实战" (chenxutan.com), the
+ * inference parameters no_repeat_ngram_size / ngram_window.]
+ *   tokens      [batch][ring_cap] int32: generated token of position pos at
+ *               pos % ring_cap (ring_cap >= window; only the last window
+ *               positions are read);
+ *   n_gen       [batch] int32: tokens generated so far;
+ *   page_tokens [batch] int32: tokens generated in the current page (read
+ *               only when max_page_tokens > 0; may be NULL otherwise);
+ *   logits      [batch][vocab], dtype UOCR_F32 or UOCR_BF16, modified in place.
+ *   Ban: inside the last min(window, n_gen) generated tokens, every n-gram
+ *   whose first ngram-1 tokens equal the last ngram-1 generated tokens sets
+ *   the logit of its last token to -inf.  Page guard (max_page_tokens > 0
+ *   and page_tokens[b] >= max_page_tokens): every logit but page_token's and
+ *   eos_token's is set to -inf.  Only -inf is written; tokens outside
+ *   [0, vocab) are ignored.  1 <= window <= 4096, ngram >= 1.             */
+int uocr_ngram_ban(int32_t batch, const int32_t* tokens, int32_t ring_cap,
+                   const int32_t* n_gen, const int32_t* page_tokens,
+                   int32_t ngram, int32_t window, int32_t page_token,
+                   int32_t eos_token, int32_t max_page_tokens, void* logits,
+                   int32_t vocab, int32_t dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * uocr_srswa_decode -- SR-SWA decode: selected blocks + window, log bias.
  * [nxmr.cn/news/162408 "稀疏路由" step 4 and "环形缓冲"; 16 x 32 = 512
  * reference tokens per query.]

@@ -370,6 +370,38 @@ int uocr_prefill_route(const uocr_shape* shape, const uocr_route* route, const v
                                                static_cast<hipStream_t>(stream)), fn);
 }
 
+int uocr_ngram_ban(int32_t batch, const int32_t* tokens, int32_t ring_cap, const int32_t* n_gen,
+                   const int32_t* page_tokens, int32_t ngram, int32_t window, int32_t page_token,
+                   int32_t eos_token, int32_t max_page_tokens, void* logits, int32_t vocab, int32_t dtype,
+                   void* stream) {
+  const char* fn = "uocr_ngram_ban";
+  if (batch < 0) return fail(UOCR_ERR_SHAPE, "%s: batch %d < 0", fn, batch);
+  if (dtype != UOCR_F32 && dtype != UOCR_BF16) return fail(UOCR_ERR_DTYPE, "%s: dtype %d", fn, dtype);
+  if (ngram < 1) return fail(UOCR_ERR_SHAPE, "%s: ngram %d < 1", fn, ngram);
+  if (window < 1 || window > uocr::kMaxNgramWindow)
+    return fail(UOCR_ERR_SHAPE, "%s: window %d outside [1, %d]", fn, window, uocr::kMaxNgramWindow);
+  if (ring_cap < window) return fail(UOCR_ERR_SHAPE, "%s: ring_cap %d < window %d", fn, ring_cap, window);
+  if (vocab < 1) return fail(UOCR_ERR_SHAPE, "%s: vocab %d < 1", fn, vocab);
+  if ((long long)batch * vocab > (1ll << 40)) return fail(UOCR_ERR_SHAPE, "%s: batch x vocab too large", fn);
+  if (max_page_tokens > 0) {
+    NEED(page_tokens, "page_tokens");
+    ALIGN4(page_tokens, "page_tokens");
+    if (page_token < 0 || page_token >= vocab || eos_token < 0 || eos_token >= vocab)
+      return fail(UOCR_ERR_SHAPE, "%s: page_token %d / eos_token %d outside [0, vocab)", fn, page_token,
+                  eos_token);
+  }
+  if (batch == 0) return ok();
+  NEED(tokens, "tokens");
+  NEED(n_gen, "n_gen");
+  NEED(logits, "logits");
+  ALIGN4(tokens, "tokens");
+  ALIGN4(n_gen, "n_gen");
+  if (dtype == UOCR_F32) ALIGN4(logits, "logits");
+  uocr::NgramArgs a{tokens, n_gen, max_page_tokens > 0 ? page_tokens : nullptr, logits, batch, ring_cap, ngram,
+                    window, page_token, eos_token, max_page_tokens, vocab};
+  return hip_status(uocr::launch_ngram_ban(dtype, a, static_cast<hipStream_t>(stream)), fn);
+}
+
 int32_t uocr_srswa_splits(const uocr_shape* shape, const uocr_route* route, int32_t num_splits) {
   if (check_shape(shape, "uocr_srswa_splits") != UOCR_OK) return -1;
   if (check_route(shape, route, "uocr_srswa_splits") != UOCR_OK) return -1;

@@ -79,6 +79,16 @@ struct PrefillArgs {
   int units, heads, prefix_cap, nb_cap, topk, tq, qt;
 };
 
+// Windowed no-repeat n-gram ban and page guard over one step's logits.
+struct NgramArgs {
+  const int32_t* tokens;      // [batch][ring_cap] generated token pos at pos % ring_cap
+  const int32_t* n_gen;       // [batch]
+  const int32_t* page_tokens; // [batch] tokens of the current page (may be null: no guard)
+  void* logits;               // [batch][vocab]
+  int batch, ring_cap, ngram, window, page_token, eos_token, max_page_tokens, vocab;
+};
+constexpr int kMaxNgramWindow = 4096;
+
 // A fused decode step: DecodeArgs plus the new token, the double-buffered
 // generated-token counts and (SR-SWA) the routing inputs and outputs.
 struct StepArgs {
@@ -110,6 +120,7 @@ hipError_t launch_block_score(int dtype, int head_dim, const ScoreArgs& a, hipSt
 hipError_t launch_entmax_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_prefill_route(int dtype, int head_dim, const PrefillArgs& a, hipStream_t s);
 int prefill_queries_per_wg(int nb_cap);
+hipError_t launch_ngram_ban(int dtype, const NgramArgs& a, hipStream_t s);
 hipError_t launch_srswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
 hipError_t launch_rswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
 

@@ -1748,6 +1748,47 @@ __global__ __launch_bounds__(kPrefillThreads) void k_prefill_fallback(PrefillArg
 }
 
 // ---------------------------------------------------------------------------
+// uocr_ngram_ban: one workgroup per sequence.  The last min(window, n_gen)
+// generated tokens go to LDS in position order; each thread takes start
+// positions p of the n-grams lying wholly in that window and compares their
+// first n-1 tokens with the last n-1 generated ones (stopping at the first
+// difference); a match writes -inf over the logit of the n-gram's last token.
+// The page guard, when on, first writes -inf over every logit but the page
+// marker's and end-of-sequence's.  Only -inf is ever written, so concurrent
+// writes of the same logit agree.
+// ---------------------------------------------------------------------------
+constexpr int kNgramThreads = 256;
+
+template <int DT>
+__global__ __launch_bounds__(kNgramThreads) void k_ngram_ban(NgramArgs a) {
+  __shared__ int hist[kMaxNgramWindow];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int T = max(a.n_gen[b], 0);
+  const int wn = min(a.window, T);
+  const int32_t* tok = a.tokens + (size_t)b * a.ring_cap;
+  for (int i = tid; i < wn; i += kNgramThreads) hist[i] = tok[(int)(((long long)T - wn + i) % a.ring_cap)];
+  auto kill = [&](int v) {
+    if (v < 0 || v >= a.vocab) return;
+    if constexpr (DT == 0)
+      reinterpret_cast<float*>(a.logits)[(size_t)b * a.vocab + v] = -INFINITY;
+    else
+      reinterpret_cast<uint16_t*>(a.logits)[(size_t)b * a.vocab + v] = 0xFF80u;  // bf16 -inf
+  };
+  if (a.page_tokens && a.max_page_tokens > 0 && a.page_tokens[b] >= a.max_page_tokens)
+    for (int v = tid; v < a.vocab; v += kNgramThreads)
+      if (v != a.page_token && v != a.eos_token) kill(v);
+  __syncthreads();
+  const int n = a.ngram;
+  if (wn < n) return;
+  const int tail = wn - n + 1;  // first of the last n-1 tokens
+  for (int p = tid; p <= wn - n; p += kNgramThreads) {
+    bool match = true;
+    for (int k = n - 2; k >= 0 && match; --k) match = hist[p + k] == hist[tail + k];  // nearest token first
+    if (match) kill(hist[p + n - 1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fused steps: append + (route +) decode in one launch
 // ---------------------------------------------------------------------------
 // uocr_srswa_step: one workgroup of NT threads per unit runs the whole step.
@@ -2069,6 +2110,14 @@ hipError_t launch_prefill_route(int dtype, int head_dim, const PrefillArgs& a, h
   long long passes = ((long long)a.units * a.tq + kPrefillThreads - 1) / kPrefillThreads;
   if (passes > 1024) passes = 1024;
   UOCR_DISPATCH(k_prefill_fallback, dim3((unsigned)passes), dim3(kPrefillThreads), a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ngram_ban(int dtype, const NgramArgs& a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  if (dtype == 0) k_ngram_ban<0><<<dim3(a.batch), dim3(kNgramThreads), 0, s>>>(a);
+  else if (dtype == 1) k_ngram_ban<1><<<dim3(a.batch), dim3(kNgramThreads), 0, s>>>(a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -253,6 +253,28 @@ def prefill_queries(w: Workload, tq: int, chunk: int = 0) -> np.ndarray:
     return store(q.astype(np.float32), w.dtype)
 
 
+def token_history(batch: int, n_tokens: int, vocab: int, seed: int, phrase: int = 40, repeat_p: float = 0.3,
+                  lookback: int = 0):
+    """Generated-token histories [batch][n_tokens] int32 with repetition, the
+    way an OCR decode loops: the text is built from random phrases of
+    `phrase` tokens, and with probability repeat_p a phrase copies an earlier
+    stretch (starting at most `lookback` tokens back when lookback > 0), so
+    long n-grams recur."""
+    g = _gen(seed, _S_MISC, 7)
+    out = np.empty((batch, n_tokens), dtype=np.int32)
+    for b in range(batch):
+        seq = []
+        while len(seq) < n_tokens:
+            if seq and g.random() < repeat_p:
+                lo = max(0, len(seq) - lookback) if lookback > 0 else 0
+                start = int(g.integers(lo, max(lo + 1, len(seq) - phrase + 1)))
+                seq.extend(seq[start:start + phrase])
+            else:
+                seq.extend(g.integers(0, vocab, size=phrase).tolist())
+        out[b] = seq[:n_tokens]
+    return out
+
+
 def step_inputs(w: Workload, step: int):
     """(q, k_new, v_new) of decode step `step`; k_new, v_new are token t0+step."""
     k, v = history_token(w, w.t0 + step)

@@ -116,6 +116,8 @@ def load_library():
         "uocr_block_score": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P]),
         "uocr_entmax15_topk": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P]),
         "uocr_prefill_route": (ctypes.c_int, [SP, RP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "uocr_ngram_ban": (ctypes.c_int, [_I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32,
+                                          _P]),
         "uocr_srswa_splits": (_I32, [SP, RP, _I32]),
         "uocr_srswa_decode": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
         "uocr_rswa_step": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P]),
@@ -135,7 +137,7 @@ def load_library():
 
 EXPORTED = ("uocr_ring_append", "uocr_rswa_splits", "uocr_rswa_workspace_bytes",
             "uocr_rswa_decode", "uocr_block_index_build", "uocr_block_score", "uocr_entmax15_topk",
-            "uocr_prefill_route",
+            "uocr_prefill_route", "uocr_ngram_ban",
             "uocr_srswa_splits", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
             "uocr_status_string", "uocr_last_error", "uocr_version")
 
@@ -279,6 +281,22 @@ def uocr_prefill_route(shape: Shape, route: Route, q, q_pos, proj, kbar, prefix_
     _call("uocr_prefill_route", ctypes.byref(shape.c()), ctypes.byref(route.c()), _ptr(q), tq, _ptr(q_pos),
           _ptr(proj), _ptr(kbar), _ptr(prefix_len), _ptr(sel_idx), _ptr(sel_prob), _ptr(sel_bias),
           _stream(stream))
+
+
+def uocr_ngram_ban(tokens, n_gen, page_tokens, logits, ngram: int, window: int, page_token: int = 0,
+                   eos_token: int = 0, max_page_tokens: int = 0, stream=None) -> None:
+    """tokens [B][ring_cap] int32 (position pos at pos % ring_cap); n_gen,
+    page_tokens [B] int32; logits [B][vocab] float32 or bfloat16, in place."""
+    B, V = int(logits.shape[0]), int(logits.shape[1]) if logits.dim() == 2 else -1
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    _check(logits, "logits", logits.dtype, (B, V))
+    _check(tokens, "tokens", torch.int32, (B, int(tokens.shape[1]) if tokens.dim() == 2 else -1))
+    _check(n_gen, "n_gen", torch.int32, (B,))
+    _check(page_tokens, "page_tokens", torch.int32, (B,), optional=max_page_tokens <= 0)
+    dt = 0 if logits.dtype == torch.float32 else 1
+    _call("uocr_ngram_ban", B, _ptr(tokens), int(tokens.shape[1]), _ptr(n_gen), _ptr(page_tokens), ngram, window,
+          page_token, eos_token, max_page_tokens, _ptr(logits), V, dt, _stream(stream))
 
 
 def uocr_srswa_decode(shape: Shape, route: Route, q, k_prefix, v_prefix, prefix_len, sel_idx, sel_bias,

@@ -119,6 +119,24 @@ def test_prefill_route_validation():
                                   None, FAKE, None) == -2    # outputs beyond 2^31 entries
 
 
+def test_ngram_ban_validation():
+    U, lib = _lib()
+    call = lambda **kw: lib.uocr_ngram_ban(*[kw.get(k, d) for k, d in [
+        ("batch", 2), ("tokens", FAKE), ("ring_cap", 128), ("n_gen", FAKE), ("page_tokens", FAKE), ("ngram", 35),
+        ("window", 128), ("page_token", 7), ("eos_token", 1), ("max_page_tokens", 0), ("logits", FAKE),
+        ("vocab", 1000), ("dtype", 0), ("stream", None)]])
+    assert call(window=129) == -2              # ring shorter than the window
+    assert call(window=0) == -2
+    assert call(window=4097, ring_cap=5000) == -2
+    assert call(ngram=0) == -2
+    assert call(dtype=5) == -3
+    assert call(max_page_tokens=10, page_tokens=None) == -1
+    assert call(max_page_tokens=10, page_token=1000) == -2
+    assert call(tokens=None) == -1
+    assert call(logits=ctypes.c_void_p(0x10002)) == -5  # float32 logits need 4-byte alignment
+    assert call(batch=0, tokens=None, n_gen=None, logits=None) == 0
+
+
 def test_split_geometry():
     U, lib = _lib()
     for B, H, m in [(64, 10, 2592), (512, 10, 288), (1, 2, 528), (32, 10, 10240), (8, 10, 32000), (1, 1, 0)]:
