@@ -64,6 +64,9 @@ def parse():
                     help="fused: one uocr_*_step launch per step; separate: one launch per row")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ngram-ban", type=int, default=0, metavar="B",
+                    help="instead of the decode step, time uocr_ngram_ban on B sequences (n = 35, window 1024, "
+                         "vocabulary 129280, float32 logits)")
     ap.add_argument("--prefill-route", type=int, default=0, metavar="TQ",
                     help="instead of the decode step, time uocr_prefill_route on a chunk of TQ queries per "
                          "(sequence, head) (the sparse workload's last TQ prefix positions)")
@@ -260,6 +263,83 @@ def prefill_main(args):
 
 
 # ----------------------------------------------------------------------------
+# no-repeat n-gram ban (a separate measurement)
+# ----------------------------------------------------------------------------
+def ngram_main(args):
+    import torch
+
+    from long_context_decode_attn_amd import synth as S
+    from long_context_decode_attn_amd import uocr as U
+
+    U.load_library()
+    B, n, W, V, T = args.ngram_ban, 35, 1024, 129280, 6144
+    hist = S.token_history(B, T, V, 11, phrase=105, repeat_p=0.5, lookback=W - 105)
+    ring = torch.from_numpy(np.ascontiguousarray(hist[:, T - W:])).cuda()   # position pos at pos % W
+    ring = torch.roll(ring, shifts=(T - W) % W, dims=1).contiguous()
+    n_gen = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    page = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    logits = [torch.randn((B, V), device="cuda") for _ in range(8)]
+
+    def run(i):
+        U.uocr_ngram_ban(ring, n_gen, page, logits[i % len(logits)], n, W, page_token=128827, eos_token=1,
+                         max_page_tokens=20000)
+
+    for i in range(20):
+        run(i)
+    torch.cuda.synchronize()
+    G, reps = 64, 40    # a HIP graph of G launches replayed: the launch rate of the host is not timed
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(G):
+            run(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    K = G * reps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    probe = torch.zeros((B, V), device="cuda")
+    U.uocr_ngram_ban(ring, n_gen, page, probe, n, W, page_token=128827, eos_token=1, max_page_tokens=20000)
+    banned = int(torch.isneginf(probe).sum().item())
+    hbm = B * (W * 4 + 8) + banned * 4
+    result = {
+        "metric": "n-gram ban sequences/s", "value": round(B / (ms * 1e-3), 1), "unit": "sequences/s",
+        "n_gpus": 1, "steps": K, "warmup": 20, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": f"ngram-ban-b{B}-n{n}-w{W}", "batch": B, "ngram": n, "window": W, "vocab": V,
+                   "generated": T, "timing": "HIP graph of 64 launches replayed 40 times between HIP events"},
+        "roofline": {"kernel": "uocr_ngram_ban", "bound": "hbm", "achieved": round(hbm / (ms * 1e-3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 6),
+                     "traffic": None},
+        "note": "latency-bound: one workgroup per sequence; the bytes are the last window of tokens",
+        "banned_logits_per_step": banned,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = ngram_cpu_baseline(hist, n, W, V, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def ngram_cpu_baseline(hist, n, W, V, budget_s):
+    """The oracle's ngram_process, one sequence at a time, until the budget
+    is spent; returns sequences/s."""
+    from oracle import uocr_oracle as O
+    logits = np.zeros(V)
+    done, spent = 0, 0.0
+    while spent < budget_s:
+        b = done % len(hist)
+        t1 = time.perf_counter()
+        O.ngram_process(logits, hist[b].tolist(), n, W, 0, 20000, 128827, 1)
+        spent += time.perf_counter() - t1
+        done += 1
+    return {"value": done / spent, "unit": "sequences/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} sequences of {len(hist[0])} generated tokens, window {W}, n {n}, python, 1 thread"}
+
+
+# ----------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1:
@@ -269,6 +349,8 @@ def main():
 
     if args.prefill_route:
         return prefill_main(args)
+    if args.ngram_ban:
+        return ngram_main(args)
 
     import torch
 

@@ -1766,7 +1766,11 @@ __global__ __launch_bounds__(kNgramThreads) void k_ngram_ban(NgramArgs a) {
   const int T = max(a.n_gen[b], 0);
   const int wn = min(a.window, T);
   const int32_t* tok = a.tokens + (size_t)b * a.ring_cap;
-  for (int i = tid; i < wn; i += kNgramThreads) hist[i] = tok[(int)(((long long)T - wn + i) % a.ring_cap)];
+  const int s0 = (T - wn) % a.ring_cap;  // slot of the window's first token
+  for (int i = tid; i < wn; i += kNgramThreads) {
+    const int slot = s0 + i;
+    hist[i] = tok[slot < a.ring_cap ? slot : slot - a.ring_cap];
+  }
   auto kill = [&](int v) {
     if (v < 0 || v >= a.vocab) return;
     if constexpr (DT == 0)
