@@ -39,12 +39,12 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("466dbe1b612e8206", 45162633, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("466dbe1b612e8206", 18867663, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("466dbe1b612e8206", 892439280, 1720749),
-    ("uocr_rswa_step", "dense-1p-b512"): ("466dbe1b612e8206", 1092083661, 3940444),
-    ("uocr_rswa_step", "dense-40p-b32"): ("466dbe1b612e8206", 1699637165, 1383423),
-    ("uocr_rswa_step", "dense-125p-b8"): ("466dbe1b612e8206", 1316342296, 1172862),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("ffc7a4954d93b1e7", 45156551, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("ffc7a4954d93b1e7", 18887117, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("ffc7a4954d93b1e7", 892437030, 1720758),
+    ("uocr_rswa_step", "dense-1p-b512"): ("ffc7a4954d93b1e7", 1092083640, 3940443),
+    ("uocr_rswa_step", "dense-40p-b32"): ("ffc7a4954d93b1e7", 1699637416, 1383410),
+    ("uocr_rswa_step", "dense-125p-b8"): ("ffc7a4954d93b1e7", 1316344520, 1172861),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
