@@ -54,3 +54,41 @@ def test_graph_replays_match_eager(sparse, fused, splits):
             assert torch.equal(g_sess.sel_idx, e_sess.sel_idx), rep
         # eager work of the program between replays
         _ = (e_sess.out.float() * 2).sum().item()
+
+
+def test_prefill_route_and_ngram_ban_in_a_graph():
+    """Prefill routing (two kernels per call) and the n-gram ban captured in a
+    graph: every replay gives the eager results."""
+    need_gpu()
+    from long_context_decode_attn_amd import uocr as U
+    w = S.Workload("graph-prefill", batch=2, heads=3, head_dim=128, dtype="bf16", pages=40, prompt=0, t0=0,
+                   steps=1, seed=21, sparse=True, planted=4, fixed_query=True)
+    say("graph prefill route + ngram ban")
+    sess = DecodeSession(w)
+    sess.build_index()
+    q = to_device(S.prefill_queries(w, 40), w.dtype)
+    pos = torch.tensor([w.prefix_len - 20, 3000], dtype=torch.int32, device="cuda")
+    eager = [t.clone() for t in sess.prefill_route(q, pos)]
+    hist = torch.from_numpy(S.token_history(4, 700, 500, 5, phrase=20, repeat_p=0.5, lookback=100)).cuda()
+    n_gen = torch.tensor([700, 650, 30, 699], dtype=torch.int32, device="cuda")
+    page = torch.tensor([0, 25, 3, 40], dtype=torch.int32, device="cuda")
+    base = torch.randn((4, 500), device="cuda")
+    ref = base.clone()
+    U.uocr_ngram_ban(hist, n_gen, page, ref, 5, 128, page_token=7, eos_token=1, max_page_tokens=25)
+    outs = [torch.empty_like(t) for t in eager]
+    lg = base.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        U.uocr_prefill_route(sess.shape, sess.route, q, pos, sess.proj, sess.kbar, sess.prefix_len, *outs)
+        U.uocr_ngram_ban(hist, n_gen, page, lg, 5, 128, page_token=7, eos_token=1, max_page_tokens=25)
+    for rep in range(4):
+        for t in outs:
+            t.fill_(-7)
+        lg.copy_(base)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
+        assert torch.equal(lg, ref), rep
+        _ = (lg.float() * 2).sum().item()   # eager work between replays
