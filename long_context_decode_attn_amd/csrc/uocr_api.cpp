@@ -109,6 +109,7 @@ size_t ws_bytes_for(int units, int splits, int head_dim) {
 
 constexpr int kDenseWaves = 4;    // waves per workgroup of the dense decode
 constexpr int kSparseWaves = 8;   // default waves per unit of the sparse decode
+constexpr int kCUs = 256;         // compute units of an MI355X
 constexpr int kMaxPrefillQueries = 1 << 20;  // queries per unit in one prefill routing call
 
 // Dense split geometry: workgroups per unit and keys per workgroup for the
@@ -121,10 +122,22 @@ void rswa_geometry(const uocr_shape* sh, int32_t req, int* splits, int* chunk) {
   if (req > 0) {
     S = req;
   } else {
-    // aim at ~2048 workgroups over the chip (256 CUs), >= 512 keys each
-    const int want = (2048 + units - 1) / units;
+    // The fewest splits (longest chunks, least merging) whose workgroups
+    // fill the 256 CUs of the chip and spread evenly over them: at least 256
+    // workgroups, and the busiest CU holds no more than 1/0.93 of the mean
+    // (measured: 480 workgroups stream at 80% of peak, 560 at 69%).  Chunks
+    // stay >= 512 keys; failing that, aim at ~2048 workgroups.
     const int cap = (L + 511) / 512;
-    S = want < cap ? want : cap;
+    S = 0;
+    for (int s = 1; s <= cap && S == 0; ++s) {
+      const long long n = (long long)units * s;
+      const long long slots = (n + kCUs - 1) / kCUs * kCUs;
+      if (n >= kCUs && n * 100 >= slots * 93) S = s;
+    }
+    if (S == 0) {
+      const int want = (2048 + units - 1) / units;
+      S = want < cap ? want : cap;
+    }
   }
   if (S > max_useful) S = max_useful;
   if (S < 1) S = 1;
