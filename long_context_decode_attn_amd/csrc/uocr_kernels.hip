@@ -576,7 +576,6 @@ __global__ __launch_bounds__(512) void k_srswa_decode(DecodeArgs a) {
   }
   const uint64_t mask = __ballot(live);
   const int n_live = __popcll(mask);
-  const int n_tasks = n_live + (w + kBlock - 1) / kBlock;
   const int grp = lane / G::LPR, c = lane % G::LPR;
 
   float q[G::E];
@@ -584,24 +583,41 @@ __global__ __launch_bounds__(512) void k_srswa_decode(DecodeArgs a) {
   State<G::E> st;
   st.init();
   const size_t cb = (size_t)c * 16;
-  for (int t = wave; t < n_tasks; t += W) {
-    if (t < n_live) {
+  // The waves are shared between the window and the live blocks in
+  // proportion to their rows, so that (up to 4 live blocks with 8 waves)
+  // every wave has all of its rows in flight at once: one HBM round trip.
+  const int R = w + kBlock * n_live;
+  int ww = R > 0 ? (W * w + R - 1) / R : 0;  // waves on the window
+  if (w > 0) ww = max(1, min(ww, n_live > 0 ? W - 1 : W));
+  const int wl = max(W - ww, 1);             // waves on the live blocks (wave 0 too when W = 1)
+  const int l0 = W - wl;                     // first of them
+  if (wave < ww) {
+    const int WR = (w + ww - 1) / ww;
+    const int r0 = wave * WR, nr = min(WR, w - r0);
+    if (nr > 0) {
+      const size_t base = ((size_t)unit * a.window + r0) * G::ROWB + cb;
+      attend_range<DT, D>(static_cast<const char*>(a.k_ring) + base,
+                          static_cast<const char*>(a.v_ring) + base, nr, 0.f, q, st, grp);
+    }
+  }
+  if (wave >= l0 && n_live > 0) {
+    // each live block cut into cpb chunks of 32 / cpb rows
+    int cpb = 1;
+    while (2 * cpb * n_live <= wl && 2 * cpb * G::RPL <= kBlock) cpb *= 2;
+    const int rpc = kBlock / cpb;
+    for (int task = wave - l0; task < n_live * cpb; task += wl) {
+      const int tk = task / cpb, sub = task - tk * cpb;
       uint64_t mm = mask;
-      for (int i = 0; i < t; ++i) mm &= mm - 1;  // drop the t lowest live entries
+      for (int i = 0; i < tk; ++i) mm &= mm - 1;  // drop the tk lowest live entries
       const int slot = __ffsll((unsigned long long)mm) - 1;
       const int j = __shfl(idx, slot);
       const float bj = __shfl(bias, slot);
-      const int r0 = j * kBlock;
+      const int r0 = j * kBlock + sub * rpc;
+      const int nr = min(rpc, m - r0);
+      if (nr <= 0) continue;
       const size_t base = ((size_t)unit * a.prefix_cap + r0) * G::ROWB + cb;
       attend_range<DT, D>(static_cast<const char*>(a.k_prefix) + base,
-                          static_cast<const char*>(a.v_prefix) + base, min(kBlock, m - r0),
-                          bj * kLog2e, q, st, grp);
-    } else {
-      const int r0 = (t - n_live) * kBlock;
-      const size_t base = ((size_t)unit * a.window + r0) * G::ROWB + cb;
-      attend_range<DT, D>(static_cast<const char*>(a.k_ring) + base,
-                          static_cast<const char*>(a.v_ring) + base, min(kBlock, w - r0), 0.f, q, st,
-                          grp);
+                          static_cast<const char*>(a.v_prefix) + base, nr, bj * kLog2e, q, st, grp);
     }
   }
   wg_finish<DT, D>(st, lds_ml, lds_o, a, unit, 0);
