@@ -39,12 +39,12 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("ffc7a4954d93b1e7", 45156551, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("ffc7a4954d93b1e7", 18887117, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("ffc7a4954d93b1e7", 892437030, 1720758),
-    ("uocr_rswa_step", "dense-1p-b512"): ("ffc7a4954d93b1e7", 1092083640, 3940443),
-    ("uocr_rswa_step", "dense-40p-b32"): ("ffc7a4954d93b1e7", 1699637416, 1383410),
-    ("uocr_rswa_step", "dense-125p-b8"): ("ffc7a4954d93b1e7", 1316344520, 1172861),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("236bd27ddcbb5181", 45166720, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("236bd27ddcbb5181", 18864564, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("236bd27ddcbb5181", 892113897, 1024670),
+    ("uocr_rswa_step", "dense-1p-b512"): ("236bd27ddcbb5181", 1092085786, 3940451),
+    ("uocr_rswa_step", "dense-40p-b32"): ("236bd27ddcbb5181", 1699311346, 686726),
+    ("uocr_rswa_step", "dense-125p-b8"): ("236bd27ddcbb5181", 1316295104, 302163),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
