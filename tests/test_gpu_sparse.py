@@ -284,3 +284,54 @@ def test_srswa_reduces_to_dense_when_every_block_is_kept():
     assert_close(to_host(sess.out), ref, "bf16", "sparse(all blocks)")
     assert_close(to_host(dense.out), ref, "bf16", "dense")
     assert np.abs(to_host(sess.out) - to_host(dense.out)).max() <= 2 ** -7
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_page_window_advance_keeps_the_ring(fused):
+    """Page-window scheduling's KV-tail carry-over: after some steps the
+    prefix is replaced by the next window of pages (new K/V, a shorter
+    prefix, the block index rebuilt) while the ring and the generated count
+    carry over; every step matches the oracle run over the same sequence of
+    prefixes and one continuous ring."""
+    need_gpu()
+    wA = _small_sparse(pages=6, prompt=0, planted=4)
+    wB = wA.replace(seed=wA.seed + 1)
+    say("page-window advance", "fused" if fused else "separate")
+    kvA, kvB = S.prefix_kv(wA), S.prefix_kv(wB)
+    ring = S.initial_ring(wA)
+    sess = DecodeSession(wA, prefix_kv=kvA, ring=ring, fused=fused)
+    host = HostMirror(wA, prefix_kv=kvA, ring=ring)
+    sess.build_index()
+    P = S.projection(wA).astype(np.float64)
+    mB = wA.prefix_len - 100
+    for step in range(6):
+        if step == 3:   # next window of pages
+            KB, VB = to_device(kvB[0], wA.dtype), to_device(kvB[1], wA.dtype)
+            sess.k_prefix.copy_(KB)
+            sess.v_prefix.copy_(VB)
+            sess.prefix_len.fill_(mB)
+            sess.build_index()
+            host.Kp, host.Vp = S.widen(kvB[0], wA.dtype), S.widen(kvB[1], wA.dtype)
+            host.prefix_len = np.full(wA.batch, mB)
+        q, kn, vn = S.step_inputs(wA, step)
+        out = to_host(sess.step(to_device(q, wA.dtype), to_device(kn, wA.dtype), to_device(vn, wA.dtype)))
+        host.append(kn, vn)
+        assert np.array_equal(sess.t_gen.cpu().numpy(), host.t_gen.astype(np.int32))
+        qd = S.widen(q, wA.dtype)
+        gi = sess.sel_idx.cpu().numpy()
+        ref, got = [], []
+        for b in range(wA.batch):
+            for h in range(wA.heads):
+                m = int(host.prefix_len[b])
+                kb = O.block_index(host.Kp[b, h], m, P)
+                s64 = O.block_scores(qd[b, h], P, kb)
+                s32 = O.as_f32(s64)
+                eps = O.score_error_bound(qd[b, h], P, kb)
+                _check_selection(gi[b, h], sess.sel_prob[b, h].cpu().numpy().astype(np.float64),
+                                 sess.sel_bias[b, h].cpu().numpy().astype(np.float64), s32, wA.topk, s64, eps,
+                                 f"step {step} unit {(b, h)}")
+                ridx, _, rbias = O.route_unit(s32, wA.topk)
+                ref.append(O.srswa_unit(qd[b, h], host.Kp[b, h], host.Vp[b, h], m, ridx, rbias,
+                                        *host.window(b, h), wA.scale))
+                got.append(out[b, h])
+        assert_close(np.stack(got), np.stack(ref), wA.dtype, f"step {step}")
