@@ -193,6 +193,16 @@ __device__ __forceinline__ int wave_sum(int x) {
          __builtin_amdgcn_readlane(x, 48);
 }
 
+// Number of (lane, e) over the wave with v[e] < T: one compare per element
+// into a lane mask and a scalar popcount, no cross-lane arithmetic.
+template <int NS>
+__device__ __forceinline__ int wave_count_below(const float (&v)[NS], float T) {
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < NS; ++e) c += __popcll(__ballot(v[e] < T));
+  return c;
+}
+
 // Exclusive prefix over the lanes of a wave of a small non-negative count
 // (< 32), from one ballot per bit: no LDS round trip.
 __device__ __forceinline__ int wave_prefix_small(int c) {
@@ -856,11 +866,24 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 constexpr int kPairMax = 256;  // largest candidate set ranked pairwise
 constexpr int kWaveBlocks = 16; // blocks per lane on the one-wave path (nb <= 1024)
 
-struct PairBuf {  // pairwise ranking (16-byte aligned rows)
-  float val[kPairMax + 4];
+struct alignas(16) PairBuf {  // pairwise ranking (16-byte aligned rows)
+  union {
+    float val[kPairMax + 4];
+    uint64_t key[(kPairMax + 4) / 2];  // one-wave path: rank_key of each block of A
+  };
   int idx[kPairMax + 4];
   int rank[kPairMax + 4];
 };
+
+// (score descending, index ascending) as one unsigned key, larger first.
+// Adding +0 turns -0 into +0, which the float order takes as equal.
+__device__ __forceinline__ uint64_t rank_key(float s, int j) {
+  return ((uint64_t)fkey(s + 0.f) << 32) | (uint32_t)~(uint32_t)j;
+}
+__device__ __forceinline__ float rank_key_score(uint64_t k) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
 
 template <int NT>
 struct __attribute__((aligned(16))) TopkSmem {
@@ -931,8 +954,10 @@ __device__ __forceinline__ double wave_sum_d(double x) {
 //
 // WIDE: a support too large for per-candidate statistics is handled here too.
 // A then only has to hold the top kk, and the threshold comes from Newton's
-// method on f(tau) = sum_j max(0, u_j - tau)^2 = 1 (convex, decreasing: from
-// tau = u_max - 1 the iterates rise monotonically to the root), followed by
+// method on h(tau) = || max(0, u - tau) ||_2 = 1 (a norm of convex functions
+// of tau, so convex, and decreasing: from tau = u_max - 1 the iterates rise
+// monotonically to the root; while the support holds still h is linear in
+// tau, where one step lands on the root), followed by
 // the closed form of the sorted algorithm on the support S = {u > tau} found,
 // accepted only if it satisfies the optimality conditions (u > tau_S on S,
 // u <= tau_S off S), which single out the exact support.
@@ -959,10 +984,7 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
   float T = 4.f;
   int nA = 0;
   for (int it = 0; it < 130; ++it) {
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < NS; ++e) c += dv[e] < T ? 1 : 0;
-    nA = wave_sum(c);
+    nA = wave_count_below(dv, T);
     if (nA >= kk) break;
     T = T * 2.f;  // reaches +inf, where every finite d counts
   }
@@ -972,10 +994,7 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
     for (int it = 0; it < 48; ++it) {
       const float mid = it == 0 ? lo : 0.5f * (lo + hi);
       if (it > 0 && !(mid > lo && mid < hi)) return false;
-      int c = 0;
-#pragma unroll
-      for (int e = 0; e < NS; ++e) c += dv[e] < mid ? 1 : 0;
-      c = wave_sum(c);
+      const int c = wave_count_below(dv, mid);
       if (c >= kk && c <= 64) {
         T = mid;
         nA = c;
@@ -1011,37 +1030,29 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
       const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
       const int cbelow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
-      if (in) {
-        pb.val[base + below] = sv[e];
-        pb.idx[base + below] = e * 64 + lane;
-      }
+      if (in) pb.key[base + below] = rank_key(sv[e], e * 64 + lane);
       if (cd) pb.rank[cbase + cbelow] = __float_as_int(sv[e]);  // candidate scores
       base += __popcll(m);
       cbase += __popcll(mc);
     }
     const int nC = cbase;
     const int nA4 = (nA + 3) & ~3, nC4 = (nC + 3) & ~3;
-    if (lane < nA4 - nA) {
-      pb.val[nA + lane] = -INFINITY;  // ranks below every block, never >= a real score
-      pb.idx[nA + lane] = 0x7fffffff;
-    }
+    if (lane < nA4 - nA) pb.key[nA + lane] = 0;  // below every block's key
     if (lane < nC4 - nC) pb.rank[nC + lane] = __float_as_int(-INFINITY);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const bool mine = lane < nA;
-    const float si = mine ? pb.val[lane] : -INFINITY;
-    const int ii = mine ? pb.idx[lane] : 0x7fffffff;
+    const uint64_t ki = mine ? pb.key[lane] : 0;
+    const float si = mine ? rank_key_score(ki) : -INFINITY;
+    const int ii = (int)~(uint32_t)ki;
     const double vi = ((double)si - dmax) * 0.5;
-    const float4* val4 = reinterpret_cast<const float4*>(pb.val);
-    const int4* idx4 = reinterpret_cast<const int4*>(pb.idx);
-    int rank = 0;
-#pragma unroll 4
+    const ulonglong2* key2 = reinterpret_cast<const ulonglong2*>(pb.key);
+    int rank = 0;  // blocks of A ahead of this lane's in (score desc, index asc)
+#pragma unroll 2
     for (int k4 = 0; k4 < nA4 / 4; ++k4) {
-      const float4 sk = val4[k4];
-      const int4 ik = idx4[k4];
-      rank += (sk.x > si || (sk.x == si && ik.x < ii)) + (sk.y > si || (sk.y == si && ik.y < ii)) +
-              (sk.z > si || (sk.z == si && ik.z < ii)) + (sk.w > si || (sk.w == si && ik.w < ii));
+      const ulonglong2 a0 = key2[2 * k4], a1 = key2[2 * k4 + 1];
+      rank += (a0.x > ki) + (a0.y > ki) + (a1.x > ki) + (a1.y > ki);
     }
     double tau;
     if (!wide) {
@@ -1053,13 +1064,12 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
         const float4 c4 = cv4[k4];
         const float ck[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (ck[k] >= si) {
-            const double vk = ((double)ck[k] - dmax) * 0.5;
-            ++r;
-            s1 += vk;
-            s2 += vk * vk;
-          }
+        for (int k = 0; k < 4; ++k) {  // branch-free: a zero adds nothing
+          const bool ge = ck[k] >= si;
+          const double vk = ge ? ((double)ck[k] - dmax) * 0.5 : 0.0;
+          r += ge;
+          s1 += vk;
+          s2 = fma(vk, vk, s2);
         }
       }
       int rr = 0;
@@ -1083,15 +1093,13 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
         double F = 0.0, G = 0.0;
 #pragma unroll
         for (int e = 0; e < NS; ++e) {
-          const double x = up[e] - t;
-          if (x > 0.0) {
-            F += x * x;
-            G += x;
-          }
+          const double x = fmax(up[e] - t, 0.0);
+          F = fma(x, x, F);
+          G += x;
         }
-        F = wave_sum_d(F);
+        F = wave_sum_d(F);  // h = sqrt(F), -h' = G / sqrt(F)
         G = wave_sum_d(G);
-        const double step = (F - 1.0) / (2.0 * G);
+        const double step = (F - sqrt(F)) / G;
         if (!(step > 0.0) || t + step == t) break;
         t += step;
       }
@@ -1561,6 +1569,7 @@ struct PrefillSmem {
   float scores[kPrefillScores];
   alignas(16) double qidx[kPrefillMaxQ][kIdxDim];
   PairBuf pb[kPrefillThreads / 64];  // one per wave
+  int next_q;                        // next query to route
 };
 
 // Query i of the tile starting at chunk query q0: position and visible blocks.
@@ -1641,46 +1650,53 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
   // 2. scores on the matrix cores, fp64: tile (16 queries) x (16 blocks),
   //    S = Qidx [16 x 32] . KBAR^T [32 x 16] in 8 steps of
   //    v_mfma_f64_16x16x4f64.  Operand layout (checked on gfx950): lane l
-  //    holds A[l % 16][k] and B[k][l % 16] with k = 4 s + l / 16 at step s;
-  //    register r of the result holds S[l / 16 + 4 r][l % 16].
+  //    holds A[l % 16][k] and B[k][l % 16] for the k of lane group l / 16 at
+  //    each step; register r of the result holds S[l / 16 + 4 r][l % 16].
+  //    Any order of the 32 index dims over (step, lane group) gives the same
+  //    sum, so lane group g takes dims 4g .. 4g+3 at steps 0-3 and 16+4g ..
+  //    16+4g+3 at steps 4-7: its key values are two 16-byte loads per tile.
   {
     typedef double v4d __attribute__((ext_vector_type(4)));
     const int lr = lane % 16, lk = lane / 16;
     double af[kIdxDim / 4];
 #pragma unroll
-    for (int st = 0; st < kIdxDim / 4; ++st) af[st] = lr < t.nq ? sm.qidx[lr][4 * st + lk] : 0.0;
+    for (int st = 0; st < kIdxDim / 4; ++st)
+      af[st] = lr < t.nq ? sm.qidx[lr][4 * lk + (st & 3) + 16 * (st >> 2)] : 0.0;
+    int vis[4];  // blocks visible to the queries of this lane's result rows
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vis[r] = lk + 4 * r < t.nq ? t.visible(lk + 4 * r) : 0;
     const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
     const int ntiles = (nbmax + 15) / 16;
-    auto load_b = [&](float (&bf)[kIdxDim / 4], int tile) {  // this lane's column of a key tile
+    auto load_b = [&](float4 (&bf)[2], int tile) {  // this lane's dims of one key of a tile
       const int j = tile * 16 + lr;
       const bool jok = j < nbmax;
-      const float* kr = K + (size_t)(jok ? j : 0) * kIdxDim + lk;
-#pragma unroll
-      for (int st = 0; st < kIdxDim / 4; ++st) bf[st] = jok ? kr[4 * st] : 0.f;
+      const float4* kr = reinterpret_cast<const float4*>(K + (size_t)(jok ? j : 0) * kIdxDim) + lk;
+      bf[0] = jok ? kr[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+      bf[1] = jok ? kr[4] : make_float4(0.f, 0.f, 0.f, 0.f);
     };
-    float bn[kIdxDim / 4];
+    float4 bn[2];
     if (wave < ntiles) load_b(bn, wave);
     for (int tile = wave; tile < ntiles; tile += W) {
       const int j = tile * 16 + lr;
-      float bf[kIdxDim / 4];
-#pragma unroll
-      for (int st = 0; st < kIdxDim / 4; ++st) bf[st] = bn[st];
+      const float4 b0 = bn[0], b1 = bn[1];
       if (tile + W < ntiles) load_b(bn, tile + W);  // next tile's keys in flight meanwhile
+      const float bf[kIdxDim / 4] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       v4d acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int st = 0; st < kIdxDim / 4; ++st)
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[st], (double)bf[st], acc, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = lk + 4 * r;
-        if (qq < t.nq && j < t.visible(qq)) sm.scores[qq * a.nb_cap + j] = (float)acc[r];
-      }
+      for (int r = 0; r < 4; ++r)
+        if (j < vis[r]) sm.scores[(lk + 4 * r) * a.nb_cap + j] = (float)acc[r];
     }
   }
+  if (tid == 0) sm.next_q = W;  // queries past the first W go to whichever wave is free
   __syncthreads();
 
-  // 3. one-wave routing
-  for (int qi = wave; qi < t.nq; qi += W) {
+  // 3. one-wave routing: wave w takes query w, then the next unclaimed one
+  //    (query costs differ a lot: a wide entmax support takes several times
+  //    as long as a planted one)
+  for (int qi = wave; qi < t.nq;) {
     const int nbq = t.visible(qi);
     const int kk = min(a.topk, nbq);
     const size_t o = ((size_t)t.unit * a.tq + t.q0 + qi) * a.topk;
@@ -1689,18 +1705,22 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
       if (a.sel_prob) a.sel_prob[o + i] = 0.f;
       a.sel_bias[o + i] = -INFINITY;
     }
-    if (kk == 0) continue;
-    const float* sq = sm.scores + qi * a.nb_cap;
-    int32_t* oi = a.sel_idx + o;
-    float* op = a.sel_prob ? a.sel_prob + o : nullptr;
-    float* ob = a.sel_bias + o;
-    bool ok = false;
-    if (nbq <= 64) ok = wave_route<1, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    else if (nbq <= 128) ok = wave_route<2, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    else if (nbq <= 256) ok = wave_route<4, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    else if (nbq <= 512) ok = wave_route<8, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    else if (nbq <= 64 * kWaveBlocks) ok = wave_route<16, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-    if (!ok && lane == 0) oi[0] = kDeferred;
+    if (kk > 0) {
+      const float* sq = sm.scores + qi * a.nb_cap;
+      int32_t* oi = a.sel_idx + o;
+      float* op = a.sel_prob ? a.sel_prob + o : nullptr;
+      float* ob = a.sel_bias + o;
+      bool ok = false;
+      if (nbq <= 64) ok = wave_route<1, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+      else if (nbq <= 128) ok = wave_route<2, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+      else if (nbq <= 256) ok = wave_route<4, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+      else if (nbq <= 512) ok = wave_route<8, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+      else if (nbq <= 64 * kWaveBlocks) ok = wave_route<16, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+      if (!ok && lane == 0) oi[0] = kDeferred;
+    }
+    int nxt = 0;  // every path through the body claims the next query
+    if (lane == 0) nxt = atomicAdd(&sm.next_q, 1);
+    qi = __shfl(nxt, 0);
   }
 }
 
