@@ -1638,11 +1638,30 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
         Qs[e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(q0)[e] << 16);
     }
     __syncthreads();
-    const int qi = tid / kIdxDim, i = tid % kIdxDim;
-    if (qi < t.nq) {
-      double acc = 0.0;
-      for (int dd = 0; dd < D; ++dd) acc += (double)Ps[dd * kIdxDim + i] * (double)Qs[qi * D + dd];
-      sm.qidx[qi][i] = acc;
+    // on the matrix cores, fp64: wave w computes the 16 x 16 tile of
+    // columns 16 (w % 2) .. + 15 over the quarter w / 2 of the D terms (same
+    // operand layout as the scores below); the four quarters are summed in a
+    // fixed order through LDS
+    typedef double v4d __attribute__((ext_vector_type(4)));
+    static_assert(kPrefillThreads == 512 && kIdxDim == 32 && kPrefillMaxQ <= 16, "q_idx tiling");
+    double* part = reinterpret_cast<double*>(sm.scores + D * kIdxDim + kPrefillMaxQ * D);  // [4][16][32]
+    {
+      const int lr = lane % 16, lk = lane / 16, c0 = 16 * (wave & 1), k0 = (wave >> 1) * (D / 4);
+      v4d acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const int dd = k0 + 4 * st + lk;
+        const double av = lr < t.nq ? (double)Qs[lr * D + dd] : 0.0;
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)Ps[dd * kIdxDim + c0 + lr], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[((wave >> 1) * 16 + lk + 4 * r) * kIdxDim + c0 + lr] = acc[r];
+    }
+    __syncthreads();
+    {
+      const int qi = tid / kIdxDim, i = tid % kIdxDim;
+      if (qi < t.nq)
+        sm.qidx[qi][i] = ((part[tid] + part[512 + tid]) + part[1024 + tid]) + part[1536 + tid];
     }
   }
   __syncthreads();
