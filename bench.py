@@ -39,12 +39,12 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("236bd27ddcbb5181", 45166720, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("236bd27ddcbb5181", 18864564, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("236bd27ddcbb5181", 892113897, 1024670),
-    ("uocr_rswa_step", "dense-1p-b512"): ("236bd27ddcbb5181", 1092085786, 3940451),
-    ("uocr_rswa_step", "dense-40p-b32"): ("236bd27ddcbb5181", 1699311346, 686726),
-    ("uocr_rswa_step", "dense-125p-b8"): ("236bd27ddcbb5181", 1316295104, 302163),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("9f0da9c740e5c9a4", 45154367, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("9f0da9c740e5c9a4", 18871770, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("9f0da9c740e5c9a4", 892108763, 1024639),
+    ("uocr_rswa_step", "dense-1p-b512"): ("9f0da9c740e5c9a4", 1092071919, 3940503),
+    ("uocr_rswa_step", "dense-40p-b32"): ("9f0da9c740e5c9a4", 1699298110, 686784),
+    ("uocr_rswa_step", "dense-125p-b8"): ("9f0da9c740e5c9a4", 1316289913, 302164),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
