@@ -422,6 +422,50 @@ def ngram_process(logits: np.ndarray, gen: Sequence[int], n: int, window: int,
 
 
 # ============================================================================
+# page2d two-axis rotary position embedding   ([SR-SWA explainer] section
+# "2D 位置编码" (rotary encoding, config sparse_rope_mode page2d, with a token
+# axis = offset within the page for the order inside a page and a page axis =
+# page number, page_mod 2, for the order between pages) and its last question
+# (the language model is DeepSeek-V2); rotary embedding itself: Su et al.,
+# "RoFormer: Enhanced Transformer with Rotary Position Embedding" (2021): its
+# 2-D case turns each pair of dimensions, its general form uses the
+# frequencies 10000^(-2(i-1)/d))
+# ============================================================================
+# Readings (the page names the two axes and page_mod only):
+# * a pair (a, b) turned by phi becomes (a cos phi - b sin phi,
+#   a sin phi + b cos phi);
+# * the pairs are (j, j + D/2), j < D/2 (the "rotate half" layout of the
+#   DeepSeek-V2 / Llama code family);
+# * pairs j < D/4 turn with the token axis, pairs j >= D/4 with the page
+#   axis; each axis has the frequencies of a rotary embedding over D/2 dims,
+#   theta_i = base^(-2 i / (D/2)) with i = j mod D/4, base 10000;
+# * token-axis position = the offset; page-axis position = page mod page_mod
+#   when page_mod > 0, else the page number.
+
+def rope_page2d_angles(page: int, offset: int, D: int, page_mod: int, base: float = 10000.0) -> np.ndarray:
+    """The angle of each of the D/2 rotation pairs for a token at (page, offset)."""
+    quarter = D // 4
+    pos_page = page % page_mod if page_mod > 0 else page
+    phi = np.empty(D // 2, dtype=F64)
+    for j in range(D // 2):
+        i = j % quarter
+        theta = float(base) ** (-2.0 * i / (D / 2))
+        pos = offset if j < quarter else pos_page
+        phi[j] = pos * theta
+    return phi
+
+
+def rope_page2d(x: np.ndarray, page: int, offset: int, page_mod: int, base: float = 10000.0) -> np.ndarray:
+    """x [..., D] of one token (any leading dims, e.g. heads), rotated; float64."""
+    x = np.asarray(x, dtype=F64)
+    D = x.shape[-1]
+    phi = rope_page2d_angles(page, offset, D, page_mod, base)
+    c, s = np.cos(phi), np.sin(phi)
+    a, b = x[..., :D // 2], x[..., D // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+# ============================================================================
 # Whole routing of a batch, and the certified-gap rule for near-ties
 # ============================================================================
 def route(q, k_prefix, prefix_len, proj, k: int, block: int = 32):

@@ -152,3 +152,35 @@ def test_ngram_window_counting_the_unmatched_tail_is_caught():
 
 def test_ngram_matching_one_token_short_is_caught():
     _fails(T.check_ngram, ngram_banned=lambda gen, n, window: O.ngram_banned(gen, max(n - 1, 1), window))
+
+
+def _rope_variant(swap_axes=False, freq_over_d=False, flip_sin=False, no_mod=False, interleaved=False):
+    def rope(x, page, offset, page_mod, base=10000.0):
+        x = np.asarray(x, dtype=np.float64)
+        D = x.shape[-1]
+        q4 = D // 4
+        pp = page if (no_mod or page_mod <= 0) else page % page_mod
+        phi = np.empty(D // 2)
+        for j in range(D // 2):
+            i = j % q4
+            theta = base ** (-2.0 * i / (D if freq_over_d else D / 2))
+            first = j < q4
+            phi[j] = (pp if first else offset) * theta if swap_axes else (offset if first else pp) * theta
+        cs, sn = np.cos(phi), np.sin(phi) * (-1.0 if flip_sin else 1.0)
+        if interleaved:
+            a, b = x[..., 0::2], x[..., 1::2]
+            out = np.empty_like(x)
+            out[..., 0::2], out[..., 1::2] = a * cs - b * sn, a * sn + b * cs
+            return out
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        return np.concatenate([a * cs - b * sn, a * sn + b * cs], axis=-1)
+    return rope
+
+
+def test_rope_variant_without_mistake_passes():
+    T.check_rope(rope_page2d=_rope_variant())
+
+
+@pytest.mark.parametrize("mistake", ["swap_axes", "freq_over_d", "flip_sin", "no_mod", "interleaved"])
+def test_rope_mistakes_are_caught(mistake):
+    _fails(T.check_rope, rope_page2d=_rope_variant(**{mistake: True}))

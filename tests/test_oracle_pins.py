@@ -511,3 +511,65 @@ def check_ngram(ngram_banned=O.ngram_banned, ngram_process=O.ngram_process):
 
 def test_ngram_ban_worked_cases_and_brute_force():
     check_ngram()
+
+
+# ----------------------------------------------------------------------------
+# page2d rotary embedding: values worked out by hand from the rotation and the
+# stated axis split, and the invariants of every rotary embedding
+# ----------------------------------------------------------------------------
+def check_rope(rope_page2d=O.rope_page2d):
+    c, s = math.cos, math.sin
+    z4 = np.zeros(4)
+    # D = 4: pair 0 = dims (0, 2) on the token axis, pair 1 = dims (1, 3) on the
+    # page axis, theta = 1 for both
+    np.testing.assert_allclose(rope_page2d(np.array([1., 0, 0, 0]), 5, 2, 0), [c(2), 0, s(2), 0], atol=1e-15)
+    np.testing.assert_allclose(rope_page2d(np.array([0., 0, 1, 0]), 5, 2, 0), [-s(2), 0, c(2), 0], atol=1e-15)
+    np.testing.assert_allclose(rope_page2d(np.array([0., 1, 0, 0]), 3, 7, 0), [0, c(3), 0, s(3)], atol=1e-15)
+    np.testing.assert_allclose(rope_page2d(np.array([0., 1, 0, 0]), 3, 7, 2), [0, c(1), 0, s(1)], atol=1e-15)
+    np.testing.assert_allclose(rope_page2d(np.array([0., 0, 0, 1]), 3, 7, 2), [0, -s(1), 0, c(1)], atol=1e-15)
+    assert np.array_equal(rope_page2d(z4, 9, 9, 0), z4)
+    # D = 8: pairs 0, 1 on the token axis with theta 1 and 10000^(-1/2) = 0.01,
+    # pairs 2, 3 on the page axis with the same two frequencies
+    e = np.eye(8)
+    np.testing.assert_allclose(rope_page2d(e[1], 0, 100, 0), c(1) * e[1] + s(1) * e[5], atol=1e-14)
+    np.testing.assert_allclose(rope_page2d(e[0], 0, 100, 0), c(100) * e[0] + s(100) * e[4], atol=1e-13)
+    np.testing.assert_allclose(rope_page2d(e[3], 100, 0, 0), c(1) * e[3] + s(1) * e[7], atol=1e-14)
+    np.testing.assert_allclose(rope_page2d(e[2], 100, 0, 0), c(100) * e[2] + s(100) * e[6], atol=1e-13)
+    np.testing.assert_allclose(rope_page2d(e[3], 100, 0, 3), c(0.01) * e[3] + s(0.01) * e[7], atol=1e-15)
+    np.testing.assert_allclose(rope_page2d(e[1], 0, 100, 0, base=100.0), c(10) * e[1] + s(10) * e[5], atol=1e-13)
+    rng = np.random.default_rng(11)
+    for D in (8, 64, 128):
+        x = rng.standard_normal((3, D))
+        # position (0, 0) and a page that page_mod maps to 0 leave x as it is
+        assert np.array_equal(rope_page2d(x, 0, 0, 2), x)
+        assert np.array_equal(rope_page2d(x, 4, 37, 2), rope_page2d(x, 0, 37, 2))
+        assert np.array_equal(rope_page2d(x, 5, 37, 2), rope_page2d(x, 1, 37, 2))
+        # every pair keeps its length, so does the vector
+        y = rope_page2d(x, 7, 1234, 0)
+        h = D // 2
+        np.testing.assert_allclose(y[:, :h] ** 2 + y[:, h:] ** 2, x[:, :h] ** 2 + x[:, h:] ** 2, rtol=1e-12)
+        # the rows (heads) are turned independently, by the same rotation
+        for r in range(3):
+            np.testing.assert_allclose(rope_page2d(x[r], 7, 1234, 0), y[r], rtol=0, atol=0)
+        # a dot product depends only on the differences of the positions
+        q, k = rng.standard_normal(D), rng.standard_normal(D)
+        for (p1, o1, p2, o2) in [(3, 40, 1, 7), (0, 5, 9, 5), (12, 0, 12, 300)]:
+            lhs = rope_page2d(q, p1, o1, 0) @ rope_page2d(k, p2, o2, 0)
+            rhs = rope_page2d(q, p1 - p2, o1 - o2, 0) @ k
+            assert abs(lhs - rhs) <= 1e-11 * (1 + abs(lhs)), (D, p1, o1, p2, o2)
+        # rotations compose by adding positions, and position (-p, -o) undoes (p, o)
+        np.testing.assert_allclose(rope_page2d(rope_page2d(x, 2, 30, 0), 5, 11, 0), rope_page2d(x, 7, 41, 0),
+                                   atol=1e-12)
+        np.testing.assert_allclose(rope_page2d(rope_page2d(x, 6, 900, 0), -6, -900, 0), x, atol=1e-12)
+        # the token axis alone moves the first half of the pairs, the page axis the second
+        a = rope_page2d(x, 0, 55, 0) - x
+        b = rope_page2d(x, 55, 0, 0) - x
+        q4 = D // 4
+        tok = np.r_[0:q4, h:h + q4]
+        pag = np.r_[q4:h, h + q4:D]
+        assert np.array_equal(a[:, pag], np.zeros_like(a[:, pag])) and np.abs(a[:, tok]).max() > 1e-3
+        assert np.array_equal(b[:, tok], np.zeros_like(b[:, tok])) and np.abs(b[:, pag]).max() > 1e-3
+
+
+def test_rope_page2d_worked_cases_and_invariants():
+    check_rope()
