@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--prefill-route", type=int, default=0, metavar="TQ",
                     help="instead of the decode step, time uocr_prefill_route on a chunk of TQ queries per "
                          "(sequence, head) (the sparse workload's last TQ prefix positions)")
+    ap.add_argument("--rope-page2d", type=int, default=0, metavar="TQ",
+                    help="instead of the decode step, time uocr_rope_page2d over the keys of a prefill chunk of TQ "
+                         "tokens per (sequence, head) of the workload (page_mod 2, base 10000)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (known bytes) so that a "
                          "counter profile of this run can scale FETCH_SIZE / WRITE_SIZE")
@@ -339,6 +342,118 @@ def ngram_cpu_baseline(hist, n, W, V, budget_s):
             "sample": f"{done} sequences of {len(hist[0])} generated tokens, window {W}, n {n}, python, 1 thread"}
 
 
+def calibration_copy():
+    """One plain 256 MiB device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of the same run."""
+    import torch
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def rope_main(args):
+    import torch
+
+    from long_context_decode_attn_amd import synth as S
+    from long_context_decode_attn_amd import uocr as U
+    from long_context_decode_attn_amd.session import to_device
+
+    U.load_library()
+    if args.copy_calibration:
+        calibration_copy()
+    w = S.WORKLOADS[args.workload]
+    B, H, D, T = w.batch, w.heads, w.head_dim, args.rope_page2d
+    tag = f"{w.name}-rope-chunk{T}"
+    shape = U.Shape.of(w)
+    page, offset = S.page_positions(5, B, T, page_tokens=400, first_page=3, start_offset=100)
+    tp, to = torch.from_numpy(page).cuda(), torch.from_numpy(offset).cuda()
+    x0 = to_device(S.rope_rows(5, B, H, T, D, w.dtype), w.dtype)
+    row_bytes = B * H * T * D * w.elem_bytes
+    # enough copies that the ones in rotation exceed the 256 MB Infinity Cache
+    nbuf = max(2, -(-3 * 256 * 2 ** 20 // row_bytes))
+    xs = [x0.clone() for _ in range(nbuf)]
+    for i in range(args.warmup):
+        U.uocr_rope_page2d(shape, xs[i % nbuf], tp, to)
+    torch.cuda.synchronize()
+    # a HIP graph of launches over the buffers in turn, replayed: the host's
+    # launch rate is not timed
+    G = nbuf * max(1, 48 // nbuf)
+    chunk_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(chunk_graph):
+        for i in range(G):
+            U.uocr_rope_page2d(shape, xs[i % nbuf], tp, to)
+    chunk_graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-args.steps // G))
+    K = G * reps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        chunk_graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    # one decode step's queries and keys (T = 1) in a HIP graph: the latency of a launch
+    q1 = torch.zeros((B, H, 1, D), dtype=x0.dtype, device="cuda")
+    p1, o1 = tp[:, :1].contiguous(), to[:, :1].contiguous()
+    for _ in range(3):
+        U.uocr_rope_page2d(shape, q1, p1, o1)
+    G1, reps1 = 64, 20
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(G1):
+            U.uocr_rope_page2d(shape, q1, p1, o1)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps1):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / (G1 * reps1) * 1e3
+    hbm = 2 * row_bytes + B * T * 8
+    gbs = hbm / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "page2d RoPE tokens/s (batch x heads x chunk tokens)", "value": round(B * H * T / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": tag, "batch": B, "heads": H, "head_dim": D, "tokens": T,
+                   "page_mod": 2, "base": 10000.0, "buffers_cycled": nbuf,
+                   "timing": f"HIP graph of {G} launches replayed {reps} times between HIP events"},
+        "roofline": {"kernel": "uocr_rope_page2d", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("uocr_rope_page2d", tag)},
+        "hbm_bytes_per_launch": hbm,
+        "decode_step_us": round(step_us, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = rope_cpu_baseline(w, page, offset, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def rope_cpu_baseline(w, page, offset, budget_s):
+    """The oracle's rope_page2d over every head of one token at a time, until
+    the budget is spent; returns tokens/s (token = one (sequence, head, position))."""
+    from long_context_decode_attn_amd import synth as S
+    from oracle import uocr_oracle as O
+    T = page.shape[1]
+    x = S.widen(S.rope_rows(5, 1, w.heads, min(T, 256), w.head_dim, w.dtype), w.dtype)[0]
+    done, spent, t = 0, 0.0, 0
+    while spent < budget_s:
+        tt = t % x.shape[1]
+        t1 = time.perf_counter()
+        O.rope_page2d(x[:, tt], int(page[0, tt]), int(offset[0, tt]), 2)
+        spent += time.perf_counter() - t1
+        done += w.heads
+        t += 1
+    return {"value": done / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{t} positions x {w.heads} heads of {w.name}, float64 numpy, 1 thread"}
+
+
 # ----------------------------------------------------------------------------
 def main():
     args = parse()
@@ -349,6 +464,8 @@ def main():
 
     if args.prefill_route:
         return prefill_main(args)
+    if args.rope_page2d:
+        return rope_main(args)
     if args.ngram_ban:
         return ngram_main(args)
 
@@ -384,13 +501,7 @@ def main():
         idx_ms = e0.elapsed_time(e1) / len(layers)
 
     if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy()
 
     pool_n = 64
     qp, kp, vp = S.step_pool(w, pool_n)

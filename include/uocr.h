@@ -232,6 +232,30 @@ int uocr_ngram_ban(int32_t batch, const int32_t* tokens, int32_t ring_cap,
                    int32_t vocab, int32_t dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * uocr_rope_page2d -- page2d two-axis rotary position embedding, in place.
+ * [nxmr.cn/news/162408, section "2D 位置编码": a rotary encoding with a token
+ * axis (offset within the page) and a page axis (page number, page_mod 2),
+ * config sparse_rope_mode page2d; the rotation of each pair of dimensions is
+ * RoFormer's (Su et al., 2021).  The page gives neither the frequencies nor
+ * the split of the head dimension: the choices below are this library's.]
+ *   x       [B][H][tokens][D] in shape->dtype (queries or keys), rotated in
+ *           place; only batch, heads, head_dim and dtype of shape are used;
+ *   page, offset [B][tokens] int32 (device): the position of token t of
+ *           sequence b, shared by its heads; negative values count as 0.
+ *   Pair j < D/2 is the dims (j, j + D/2); (a, b) becomes
+ *   (a cos phi - b sin phi, a sin phi + b cos phi).  Pairs j < D/4 take
+ *   phi = offset * theta_j, pairs j >= D/4 take phi = pp * theta_(j - D/4)
+ *   with pp = page mod page_mod (page_mod > 0) or page (page_mod = 0), and
+ *   theta_i = base^(-2 i / (D/2)).  The angle is exact to ~1e-10 rad; cos,
+ *   sin and the rotation are fp32, bf16 results rounded to nearest even.
+ *   0 <= tokens <= 2^20, page_mod >= 0, base finite and > 0 (else
+ *   UOCR_ERR_SHAPE); tokens = 0 does nothing.  x 16-byte aligned.  One
+ *   launch on `stream`.                                                   */
+int uocr_rope_page2d(const uocr_shape* shape, void* x, int32_t tokens,
+                     const int32_t* page, const int32_t* offset,
+                     int32_t page_mod, float base, void* stream);
+
+/* ---------------------------------------------------------------------------
  * uocr_srswa_decode -- SR-SWA decode: selected blocks + window, log bias.
  * [nxmr.cn/news/162408 "稀疏路由" step 4 and "环形缓冲"; 16 x 32 = 512
  * reference tokens per query.]

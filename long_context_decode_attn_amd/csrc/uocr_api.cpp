@@ -415,6 +415,27 @@ int uocr_ngram_ban(int32_t batch, const int32_t* tokens, int32_t ring_cap, const
   return hip_status(uocr::launch_ngram_ban(dtype, a, static_cast<hipStream_t>(stream)), fn);
 }
 
+int uocr_rope_page2d(const uocr_shape* shape, void* x, int32_t tokens, const int32_t* page,
+                     const int32_t* offset, int32_t page_mod, float base, void* stream) {
+  const char* fn = "uocr_rope_page2d";
+  CHECK(check_shape(shape, fn));
+  if (tokens < 0 || tokens > kMaxPrefix) return fail(UOCR_ERR_SHAPE, "%s: tokens %d outside [0, 2^20]", fn, tokens);
+  if (page_mod < 0) return fail(UOCR_ERR_SHAPE, "%s: page_mod %d < 0", fn, page_mod);
+  if (!std::isfinite(base) || !(base > 0.f)) return fail(UOCR_ERR_SHAPE, "%s: base must be finite and > 0", fn);
+  if ((int64_t)shape->batch * ((tokens + uocr::kRopeTokens - 1) / uocr::kRopeTokens) >= (int64_t(1) << 31))
+    return fail(UOCR_ERR_SHAPE, "%s: batch x tokens too large", fn);
+  if (tokens == 0) return ok();
+  NEED(x, "x");
+  NEED(page, "page");
+  NEED(offset, "offset");
+  ALIGN16(x, "x");
+  ALIGN4(page, "page");
+  ALIGN4(offset, "offset");
+  uocr::RopeArgs a{x, page, offset, shape->batch, shape->heads, tokens, page_mod, base};
+  return hip_status(uocr::launch_rope_page2d(shape->dtype, shape->head_dim, a, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int32_t uocr_srswa_splits(const uocr_shape* shape, const uocr_route* route, int32_t num_splits) {
   if (check_shape(shape, "uocr_srswa_splits") != UOCR_OK) return -1;
   if (check_route(shape, route, "uocr_srswa_splits") != UOCR_OK) return -1;

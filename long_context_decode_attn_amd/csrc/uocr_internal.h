@@ -89,6 +89,17 @@ struct NgramArgs {
 };
 constexpr int kMaxNgramWindow = 4096;
 
+// page2d rotary embedding of x [batch][heads][tokens][D], in place, with the
+// positions of token t of sequence b at page[b * tokens + t], offset[...].
+constexpr int kRopeTokens = 16;  // tokens of one sequence per workgroup
+struct RopeArgs {
+  void* x;
+  const int32_t* page;
+  const int32_t* offset;
+  int batch, heads, tokens, page_mod;
+  float base;
+};
+
 // A fused decode step: DecodeArgs plus the new token, the double-buffered
 // generated-token counts and (SR-SWA) the routing inputs and outputs.
 struct StepArgs {
@@ -121,6 +132,7 @@ hipError_t launch_entmax_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_prefill_route(int dtype, int head_dim, const PrefillArgs& a, hipStream_t s);
 int prefill_queries_per_wg(int nb_cap);
 hipError_t launch_ngram_ban(int dtype, const NgramArgs& a, hipStream_t s);
+hipError_t launch_rope_page2d(int dtype, int head_dim, const RopeArgs& a, hipStream_t s);
 hipError_t launch_srswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
 hipError_t launch_rswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
 

@@ -2080,6 +2080,138 @@ __global__ __launch_bounds__(1024) void k_rswa_step(StepArgs a) {
   wg_finish<DT, D>(st, lds_ml, lds_o, d, unit, split);
 }
 
+// ---------------------------------------------------------------------------
+// uocr_rope_page2d: page2d two-axis rotary embedding, in place.  Pair j of a
+// row is (j, j + D/2); pairs j < D/4 turn by offset * theta_j, the others by
+// (page mod page_mod) * theta_(j - D/4), theta_i = base^(-2 i / (D/2)).  A
+// workgroup takes up to kRopeTokens tokens of one sequence and every head.
+// Each thread first issues the loads of its first kRopeInFlight chunk pairs
+// (a 16-byte chunk of the first half of a row and the matching chunk of the
+// second half), then, while they are in flight, computes the (cos, sin) of
+// its (token, pair) entries into LDS; after the barrier it turns its chunks
+// and stores them.  The angle is formed in fp64 and brought into [-pi, pi]
+// by Cody-Waite reduction with 2 pi split in two doubles (exact to ~1e-10 rad
+// for positions below 2^24); cos and sin are then taken in fp32, and the
+// pairs are turned in fp32.  x is streamed with nontemporal loads and stores.
+// ---------------------------------------------------------------------------
+constexpr int kRopeThreads = 256;
+constexpr int kRopeInFlight = 8;                       // chunk pairs per thread in flight
+constexpr double kTwoPiHi = 6.283185307179586;        // 2 pi rounded to a double
+constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
+constexpr double kInvTwoPi = 0.15915494309189535;     // 1 / (2 pi) rounded
+
+__device__ __forceinline__ void st16_stream(char* p, const uint4& v) {
+  __builtin_nontemporal_store(v4u32{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u32*>(p));
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kRopeThreads) void k_rope_page2d(RopeArgs a) {
+  using G = Geo<DT, D>;
+  constexpr int H2 = D / 2, Q4 = D / 4;
+  constexpr int CPH = H2 / G::E;                        // 16-byte chunks per half row
+  constexpr int AE = kRopeTokens * H2 / kRopeThreads;   // (token, pair) entries per thread
+  static_assert(kRopeThreads % H2 == 0 && AE >= 1, "every entry of a thread has the same pair");
+  __shared__ float2 cs[kRopeTokens][H2];
+  const int tid = threadIdx.x;
+  const int tiles = (a.tokens + kRopeTokens - 1) / kRopeTokens;
+  const int b = blockIdx.x / tiles, t0 = (blockIdx.x - b * tiles) * kRopeTokens;
+  const int nt = min(kRopeTokens, a.tokens - t0);
+  const long long n = (long long)a.heads * nt * CPH;    // chunk pairs of the workgroup
+  char* const xb = static_cast<char*>(a.x) + ((size_t)b * a.heads * a.tokens + t0) * G::ROWB;
+  auto chunk = [&](long long e) -> char* {              // first-half chunk of chunk pair e
+    const int row = (int)(e / CPH), c = (int)(e % CPH);
+    const int h = row / nt, ti = row - h * nt;
+    return xb + ((size_t)h * a.tokens + ti) * G::ROWB + c * 16;
+  };
+  // positions of this thread's entries: token tid / H2 + k (kRopeThreads / H2), pair tid % H2
+  const int j = tid % H2;
+  int pos[AE];
+#pragma unroll
+  for (int k = 0; k < AE; ++k) {
+    const int ti = tid / H2 + k * (kRopeThreads / H2);
+    pos[k] = 0;
+    if (ti < nt) {
+      const size_t pi = (size_t)b * a.tokens + t0 + ti;
+      const int pg = max(a.page[pi], 0), off = max(a.offset[pi], 0);
+      pos[k] = j < Q4 ? off : (a.page_mod > 0 ? pg % a.page_mod : pg);
+    }
+  }
+  uint4 u0[kRopeInFlight], u1[kRopeInFlight];
+#pragma unroll
+  for (int k = 0; k < kRopeInFlight; ++k) {
+    const long long e = tid + (long long)k * kRopeThreads;
+    if (e < n) {
+      const char* p = chunk(e);
+      u0[k] = ld16_stream(p);
+      u1[k] = ld16_stream(p + G::ROWB / 2);
+    }
+  }
+  const double theta = pow((double)a.base, -2.0 * (double)(j < Q4 ? j : j - Q4) / (double)H2);
+#pragma unroll
+  for (int k = 0; k < AE; ++k) {
+    const int ti = tid / H2 + k * (kRopeThreads / H2);
+    const double phi = (double)pos[k] * theta;
+    const double q = rint(phi * kInvTwoPi);
+    const double r = fma(-q, kTwoPiLo, fma(-q, kTwoPiHi, phi));
+    float sn, cn;
+    sincosf((float)r, &sn, &cn);
+    cs[ti][j] = make_float2(cn, sn);
+  }
+  __syncthreads();
+  auto turn = [&](const uint4& v0, const uint4& v1, long long e) {
+    char* p = chunk(e);
+    const int row = (int)(e / CPH), c = (int)(e % CPH);
+    const int ti = row % nt;
+    float x0[G::E], x1[G::E];
+    unpack(v0, x0);
+    unpack(v1, x1);
+#pragma unroll
+    for (int i = 0; i < G::E; ++i) {
+      const float2 w = cs[ti][c * G::E + i];
+      const float s0 = x0[i], s1 = x1[i];
+      x0[i] = fmaf(s0, w.x, -s1 * w.y);
+      x1[i] = fmaf(s0, w.y, s1 * w.x);
+    }
+    if constexpr (DT == 0) {
+      st16_stream(p, make_uint4(__float_as_uint(x0[0]), __float_as_uint(x0[1]), __float_as_uint(x0[2]),
+                                __float_as_uint(x0[3])));
+      st16_stream(p + G::ROWB / 2, make_uint4(__float_as_uint(x1[0]), __float_as_uint(x1[1]),
+                                              __float_as_uint(x1[2]), __float_as_uint(x1[3])));
+    } else {
+      uint32_t w0[4], w1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w0[i] = bf16_bits(x0[2 * i]) | (bf16_bits(x0[2 * i + 1]) << 16);
+        w1[i] = bf16_bits(x1[2 * i]) | (bf16_bits(x1[2 * i + 1]) << 16);
+      }
+      st16_stream(p, make_uint4(w0[0], w0[1], w0[2], w0[3]));
+      st16_stream(p + G::ROWB / 2, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kRopeInFlight; ++k) {
+    const long long e = tid + (long long)k * kRopeThreads;
+    if (e < n) turn(u0[k], u1[k], e);
+  }
+  // workgroups with more chunk pairs than one round (many heads, or fp32)
+  for (long long e0 = (long long)kRopeInFlight * kRopeThreads; e0 < n; e0 += (long long)kRopeInFlight * kRopeThreads) {
+#pragma unroll
+    for (int k = 0; k < kRopeInFlight; ++k) {
+      const long long e = e0 + tid + (long long)k * kRopeThreads;
+      if (e < n) {
+        const char* p = chunk(e);
+        u0[k] = ld16_stream(p);
+        u1[k] = ld16_stream(p + G::ROWB / 2);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kRopeInFlight; ++k) {
+      const long long e = e0 + tid + (long long)k * kRopeThreads;
+      if (e < n) turn(u0[k], u1[k], e);
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -2176,6 +2308,17 @@ hipError_t launch_ngram_ban(int dtype, const NgramArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   if (dtype == 0) k_ngram_ban<0><<<dim3(a.batch), dim3(kNgramThreads), 0, s>>>(a);
   else if (dtype == 1) k_ngram_ban<1><<<dim3(a.batch), dim3(kNgramThreads), 0, s>>>(a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_page2d(int dtype, int head_dim, const RopeArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.heads == 0 || a.tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.batch * ((a.tokens + kRopeTokens - 1) / kRopeTokens)));
+  if (dtype == 0 && head_dim == 64) k_rope_page2d<0, 64><<<grid, kRopeThreads, 0, s>>>(a);
+  else if (dtype == 0 && head_dim == 128) k_rope_page2d<0, 128><<<grid, kRopeThreads, 0, s>>>(a);
+  else if (dtype == 1 && head_dim == 64) k_rope_page2d<1, 64><<<grid, kRopeThreads, 0, s>>>(a);
+  else if (dtype == 1 && head_dim == 128) k_rope_page2d<1, 128><<<grid, kRopeThreads, 0, s>>>(a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

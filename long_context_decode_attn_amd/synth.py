@@ -335,3 +335,30 @@ def random_selection(seed: int, units: int, n_blocks: int, k: int, live: int):
         order = g.permutation(len(sel))[:live]
         bias[u, order] = g.uniform(-5.0, 0.0, size=len(order)).astype(np.float32)
     return idx, bias
+
+
+def rope_rows(seed: int, batch: int, heads: int, tokens: int, head_dim: int, dtype: str) -> np.ndarray:
+    """Rows to be rotated (queries or keys), storage array [B][H][T][D], N(0, 1)."""
+    return store(normal32(seed, (batch, heads, tokens, head_dim), _S_MISC, 2), dtype)
+
+
+def page_positions(seed: int, batch: int, tokens: int, page_tokens: int = 256, first_page: int = 0,
+                   start_offset: int = 0):
+    """(page, offset) int32 [B][T] of T consecutive tokens of a multi-page
+    document: each page holds a number of tokens drawn from
+    U[page_tokens/2, 3 page_tokens/2]; the offset restarts at 0 on every new
+    page.  Sequence b starts on page first_page + b at offset start_offset."""
+    g = _gen(seed, _S_MISC, 3)
+    page = np.empty((batch, tokens), dtype=np.int32)
+    offset = np.empty((batch, tokens), dtype=np.int32)
+    lo, hi = max(1, page_tokens // 2), max(1, page_tokens // 2) + page_tokens
+    for b in range(batch):
+        p, o = first_page + b, start_offset
+        length = max(int(g.integers(lo, hi + 1)), o + 1)
+        for t in range(tokens):
+            if o >= length:
+                p, o = p + 1, 0
+                length = int(g.integers(lo, hi + 1))
+            page[b, t], offset[b, t] = p, o
+            o += 1
+    return page, offset

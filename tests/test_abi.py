@@ -137,6 +137,30 @@ def test_ngram_ban_validation():
     assert call(batch=0, tokens=None, n_gen=None, logits=None) == 0
 
 
+def test_rope_page2d_validation():
+    U, lib = _lib()
+    sh = _shape(U)
+
+    def call(sh=sh, x=FAKE, tokens=64, page=FAKE, offset=FAKE, page_mod=2, base=10000.0):
+        return lib.uocr_rope_page2d(ctypes.byref(sh), x, tokens, page, offset, page_mod, base, None)
+
+    assert call(tokens=-1) == -2
+    assert call(tokens=(1 << 20) + 1) == -2
+    assert call(page_mod=-1) == -2
+    assert call(base=0.0) == -2
+    assert call(base=float("nan")) == -2
+    assert call(base=float("inf")) == -2
+    assert call(x=None) == -1
+    assert call(page=None) == -1
+    assert call(offset=None) == -1
+    assert call(x=ODD) == -5                    # rows are read as 16-byte chunks
+    assert call(page=ctypes.c_void_p(0x10002)) == -5
+    assert call(sh=_shape(U, head_dim=96)) == -6
+    assert call(sh=_shape(U, dtype=3)) == -3
+    assert call(tokens=0, x=None, page=None, offset=None) == 0   # nothing to do
+    assert lib.uocr_rope_page2d(None, FAKE, 4, FAKE, FAKE, 2, 10000.0, None) == -1
+
+
 def test_split_geometry():
     U, lib = _lib()
     for B, H, m in [(64, 10, 2592), (512, 10, 288), (1, 2, 528), (32, 10, 10240), (8, 10, 32000), (1, 1, 0)]:

@@ -1,0 +1,115 @@
+"""GPU parity of the page2d two-axis rotary embedding (uocr_rope_page2d)
+against the oracle, through the C ABI.  fp32 results must agree to 1e-5
+(the kernel takes cos and sin in fp32 of an fp64-reduced angle); bf16 results
+must be the oracle's value rounded to bf16, or its neighbour when the exact
+value lies within fp32 rounding of a tie."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_attn_amd import synth as S
+from long_context_decode_attn_amd import uocr as U
+from long_context_decode_attn_amd.session import to_device, to_host
+from oracle import uocr_oracle as O
+from tests._gpu_common import assert_close, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(x64, page, offset, page_mod, base, tokens_sample=None):
+    """Oracle rotation of x64 [B][H][T][D] (float64) token by token."""
+    B, H, T, D = x64.shape
+    out = np.empty_like(x64)
+    sample = [(b, t) for b in range(B) for t in range(T)] if tokens_sample is None else tokens_sample
+    for b, t in sample:
+        out[b, :, t] = O.rope_page2d(x64[b, :, t], int(page[b, t]), int(offset[b, t]), page_mod, base)
+    return out
+
+
+def _check(got, want, dtype, what):
+    if dtype == "f32":
+        err = np.abs(got - want).max() if got.size else 0.0
+        assert err <= 1e-5, f"{what}: max-abs {err:.3e}"
+    else:
+        # within half a bf16 ulp of the exact value, plus what fp32 rounding
+        # before the bf16 rounding can move it
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 2.0 ** -126))) - 7)
+        bad = np.abs(got - want) > 0.5 * ulp + 1e-6 * (1 + np.abs(want))
+        assert not bad.any(), f"{what}: {int(bad.sum())} elements off by more than half a bf16 ulp"
+    assert_close(got, want, dtype, what)
+
+
+def _run(B, H, T, D, dtype, page_mod=2, base=10000.0, page_tokens=256, first_page=0, start_offset=0,
+         seed=1, sample=None, page=None, offset=None):
+    say("rope", B, H, T, D, dtype, page_mod, base, first_page, start_offset)
+    x = S.rope_rows(seed, B, H, T, D, dtype)
+    if page is None:
+        page, offset = S.page_positions(seed, B, T, page_tokens, first_page, start_offset)
+    shape = U.Shape(B, H, D, 0, dtype=U.UOCR_F32 if dtype == "f32" else U.UOCR_BF16)
+    tx = to_device(x, dtype)
+    U.uocr_rope_page2d(shape, tx, torch.from_numpy(page).cuda(), torch.from_numpy(offset).cuda(), page_mod, base)
+    torch.cuda.synchronize()
+    got = to_host(tx)
+    x64 = S.widen(x, dtype)
+    clamp = lambda a: np.maximum(a, 0)
+    want = _oracle(x64, clamp(page), clamp(offset), page_mod, base, sample)
+    if sample is not None:
+        idx = tuple(np.array(sample).T)
+        got, want = got[idx[0], :, idx[1]], want[idx[0], :, idx[1]]
+    return got, want
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_matches_oracle(dtype, D):
+    need_gpu()
+    got, want = _run(3, 4, 37, D, dtype)            # 16-token tiles with a ragged last tile
+    _check(got, want, dtype, f"rope {dtype} D={D}")
+
+
+@pytest.mark.parametrize("page_mod", [0, 2, 3])
+def test_rope_page_mod(page_mod):
+    need_gpu()
+    got, want = _run(2, 3, 50, 128, "f32", page_mod=page_mod, page_tokens=8, first_page=5)
+    _check(got, want, "f32", f"page_mod={page_mod}")
+
+
+def test_rope_large_positions_keep_the_angle():
+    """Offsets near 2^20 and page numbers near 10^6 (page_mod 0): angles of
+    up to ~10^6 rad still come out exact to fp32."""
+    need_gpu()
+    got, want = _run(2, 2, 40, 128, "f32", page_mod=0, page_tokens=1 << 21, first_page=999_000,
+                     start_offset=(1 << 20) - 60)
+    _check(got, want, "f32", "large positions")
+
+
+def test_rope_other_base_and_decode_shape():
+    need_gpu()
+    got, want = _run(32, 10, 1, 128, "bf16", base=500000.0, first_page=3, start_offset=17)   # one decode step
+    _check(got, want, "bf16", "decode step, base 5e5")
+
+
+def test_rope_negative_positions_count_as_zero_and_empty_is_a_no_op():
+    need_gpu()
+    B, H, T, D = 2, 2, 20, 64
+    page = np.full((B, T), -3, np.int32)
+    offset = np.tile(np.arange(-10, 10, dtype=np.int32), (B, 1))
+    got, want = _run(B, H, T, D, "f32", page=page, offset=offset)
+    _check(got, want, "f32", "negative positions")
+    shape = U.Shape(B, H, D, 0, dtype=U.UOCR_F32)
+    x = torch.ones((B, H, 0, D), device="cuda")
+    z = torch.zeros((B, 0), dtype=torch.int32, device="cuda")
+    U.uocr_rope_page2d(shape, x, z, z)
+    torch.cuda.synchronize()
+
+
+def test_rope_prefill_chunk_shape_sampled():
+    """The bench's launch: 32 sequences x 10 heads x 2048 tokens, D = 128,
+    bf16; 300 sampled tokens, every head, against the oracle."""
+    need_gpu()
+    B, T = 32, 2048
+    rng = np.random.default_rng(9)
+    sample = sorted({(int(b), int(t)) for b, t in zip(rng.integers(0, B, 300), rng.integers(0, T, 300))})
+    sample += [(0, 0), (B - 1, T - 1)]
+    got, want = _run(B, 10, T, 128, "bf16", page_tokens=400, first_page=2, start_offset=100, sample=sample)
+    _check(got, want, "bf16", "prefill chunk")
