@@ -39,12 +39,13 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("9f0da9c740e5c9a4", 45154367, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("9f0da9c740e5c9a4", 18871770, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("9f0da9c740e5c9a4", 892108763, 1024639),
-    ("uocr_rswa_step", "dense-1p-b512"): ("9f0da9c740e5c9a4", 1092071919, 3940503),
-    ("uocr_rswa_step", "dense-40p-b32"): ("9f0da9c740e5c9a4", 1699298110, 686784),
-    ("uocr_rswa_step", "dense-125p-b8"): ("9f0da9c740e5c9a4", 1316289913, 302164),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("a713ec93c82712cf", 45138034, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("a713ec93c82712cf", 18835927, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("a713ec93c82712cf", 892115251, 1024662),
+    ("uocr_rswa_step", "dense-1p-b512"): ("a713ec93c82712cf", 1092083446, 3940443),
+    ("uocr_rswa_step", "dense-40p-b32"): ("a713ec93c82712cf", 1699311085, 686692),
+    ("uocr_rswa_step", "dense-125p-b8"): ("a713ec93c82712cf", 1316296546, 302160),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("a713ec93c82712cf", 169070021, 167798318),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
