@@ -398,16 +398,18 @@ def rope_main(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
-    # one decode step's queries and keys (T = 1) in a HIP graph: the latency of a launch
+    # one decode step's queries and keys (T = 1, one launch for both) in a HIP
+    # graph: the latency of a launch
     q1 = torch.zeros((B, H, 1, D), dtype=x0.dtype, device="cuda")
+    k1 = torch.zeros_like(q1)
     p1, o1 = tp[:, :1].contiguous(), to[:, :1].contiguous()
     for _ in range(3):
-        U.uocr_rope_page2d(shape, q1, p1, o1)
+        U.uocr_rope_page2d(shape, q1, p1, o1, y=k1)
     G1, reps1 = 64, 20
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for _ in range(G1):
-            U.uocr_rope_page2d(shape, q1, p1, o1)
+            U.uocr_rope_page2d(shape, q1, p1, o1, y=k1)
     graph.replay()
     torch.cuda.synchronize()
     e0.record()

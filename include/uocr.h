@@ -240,6 +240,9 @@ int uocr_ngram_ban(int32_t batch, const int32_t* tokens, int32_t ring_cap,
  * the split of the head dimension: the choices below are this library's.]
  *   x       [B][H][tokens][D] in shape->dtype (queries or keys), rotated in
  *           place; only batch, heads, head_dim and dtype of shape are used;
+ *   y       NULL, or a second tensor of the same layout turned by the same
+ *           positions in the same launch (e.g. x = q, y = k_new of a decode
+ *           step); it must not be x;
  *   page, offset [B][tokens] int32 (device): the position of token t of
  *           sequence b, shared by its heads; negative values count as 0.
  *   Pair j < D/2 is the dims (j, j + D/2); (a, b) becomes
@@ -248,10 +251,10 @@ int uocr_ngram_ban(int32_t batch, const int32_t* tokens, int32_t ring_cap,
  *   with pp = page mod page_mod (page_mod > 0) or page (page_mod = 0), and
  *   theta_i = base^(-2 i / (D/2)).  The angle is exact to ~1e-10 rad; cos,
  *   sin and the rotation are fp32, bf16 results rounded to nearest even.
- *   0 <= tokens <= 2^20, page_mod >= 0, base finite and > 0 (else
- *   UOCR_ERR_SHAPE); tokens = 0 does nothing.  x 16-byte aligned.  One
- *   launch on `stream`.                                                   */
-int uocr_rope_page2d(const uocr_shape* shape, void* x, int32_t tokens,
+ *   0 <= tokens <= 2^20, page_mod >= 0, base finite and > 0, y != x (else
+ *   UOCR_ERR_SHAPE); tokens = 0 does nothing.  x and y 16-byte aligned.
+ *   One launch on `stream`.                                               */
+int uocr_rope_page2d(const uocr_shape* shape, void* x, void* y, int32_t tokens,
                      const int32_t* page, const int32_t* offset,
                      int32_t page_mod, float base, void* stream);
 

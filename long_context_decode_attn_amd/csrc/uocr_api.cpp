@@ -415,7 +415,7 @@ int uocr_ngram_ban(int32_t batch, const int32_t* tokens, int32_t ring_cap, const
   return hip_status(uocr::launch_ngram_ban(dtype, a, static_cast<hipStream_t>(stream)), fn);
 }
 
-int uocr_rope_page2d(const uocr_shape* shape, void* x, int32_t tokens, const int32_t* page,
+int uocr_rope_page2d(const uocr_shape* shape, void* x, void* y, int32_t tokens, const int32_t* page,
                      const int32_t* offset, int32_t page_mod, float base, void* stream) {
   const char* fn = "uocr_rope_page2d";
   CHECK(check_shape(shape, fn));
@@ -429,9 +429,11 @@ int uocr_rope_page2d(const uocr_shape* shape, void* x, int32_t tokens, const int
   NEED(page, "page");
   NEED(offset, "offset");
   ALIGN16(x, "x");
+  if (y) ALIGN16(y, "y");
   ALIGN4(page, "page");
   ALIGN4(offset, "offset");
-  uocr::RopeArgs a{x, page, offset, shape->batch, shape->heads, tokens, page_mod, base};
+  if (y == x) return fail(UOCR_ERR_SHAPE, "%s: y is x (each tensor would be turned twice)", fn);
+  uocr::RopeArgs a{x, y, page, offset, shape->batch, shape->heads, tokens, page_mod, base};
   return hip_status(uocr::launch_rope_page2d(shape->dtype, shape->head_dim, a, static_cast<hipStream_t>(stream)),
                     fn);
 }

@@ -89,11 +89,13 @@ struct NgramArgs {
 };
 constexpr int kMaxNgramWindow = 4096;
 
-// page2d rotary embedding of x [batch][heads][tokens][D], in place, with the
-// positions of token t of sequence b at page[b * tokens + t], offset[...].
+// page2d rotary embedding of x and (if not null) y, both [batch][heads][tokens][D],
+// in place, with the positions of token t of sequence b at page[b * tokens + t],
+// offset[...].
 constexpr int kRopeTokens = 16;  // tokens of one sequence per workgroup
 struct RopeArgs {
   void* x;
+  void* y;
   const int32_t* page;
   const int32_t* offset;
   int batch, heads, tokens, page_mod;

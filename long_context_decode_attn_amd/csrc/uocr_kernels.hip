@@ -2084,7 +2084,8 @@ __global__ __launch_bounds__(1024) void k_rswa_step(StepArgs a) {
 // uocr_rope_page2d: page2d two-axis rotary embedding, in place.  Pair j of a
 // row is (j, j + D/2); pairs j < D/4 turn by offset * theta_j, the others by
 // (page mod page_mod) * theta_(j - D/4), theta_i = base^(-2 i / (D/2)).  A
-// workgroup takes up to kRopeTokens tokens of one sequence and every head.
+// workgroup takes up to kRopeTokens tokens of one sequence, every head, and
+// both tensors when a second one (y, e.g. the keys beside the queries) is given.
 // Each thread first issues the loads of its first kRopeInFlight chunk pairs
 // (a 16-byte chunk of the first half of a row and the matching chunk of the
 // second half), then, while they are in flight, computes the (cos, sin) of
@@ -2116,12 +2117,20 @@ __global__ __launch_bounds__(kRopeThreads) void k_rope_page2d(RopeArgs a) {
   const int tiles = (a.tokens + kRopeTokens - 1) / kRopeTokens;
   const int b = blockIdx.x / tiles, t0 = (blockIdx.x - b * tiles) * kRopeTokens;
   const int nt = min(kRopeTokens, a.tokens - t0);
-  const long long n = (long long)a.heads * nt * CPH;    // chunk pairs of the workgroup
-  char* const xb = static_cast<char*>(a.x) + ((size_t)b * a.heads * a.tokens + t0) * G::ROWB;
+  const long long n1 = (long long)a.heads * nt * CPH;   // chunk pairs of one tensor
+  const long long n = a.y ? 2 * n1 : n1;                 // ... of the workgroup
+  const size_t base_off = ((size_t)b * a.heads * a.tokens + t0) * G::ROWB;
+  char* const xb = static_cast<char*>(a.x) + base_off;
+  char* const yb = a.y ? static_cast<char*>(a.y) + base_off : nullptr;
   auto chunk = [&](long long e) -> char* {              // first-half chunk of chunk pair e
+    char* tb = xb;
+    if (e >= n1) {
+      tb = yb;
+      e -= n1;
+    }
     const int row = (int)(e / CPH), c = (int)(e % CPH);
     const int h = row / nt, ti = row - h * nt;
-    return xb + ((size_t)h * a.tokens + ti) * G::ROWB + c * 16;
+    return tb + ((size_t)h * a.tokens + ti) * G::ROWB + c * 16;
   };
   // positions of this thread's entries: token tid / H2 + k (kRopeThreads / H2), pair tid % H2
   const int j = tid % H2;
@@ -2160,7 +2169,8 @@ __global__ __launch_bounds__(kRopeThreads) void k_rope_page2d(RopeArgs a) {
   __syncthreads();
   auto turn = [&](const uint4& v0, const uint4& v1, long long e) {
     char* p = chunk(e);
-    const int row = (int)(e / CPH), c = (int)(e % CPH);
+    const long long et = e >= n1 ? e - n1 : e;
+    const int row = (int)(et / CPH), c = (int)(et % CPH);
     const int ti = row % nt;
     float x0[G::E], x1[G::E];
     unpack(v0, x0);

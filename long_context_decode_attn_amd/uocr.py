@@ -118,7 +118,7 @@ def load_library():
         "uocr_prefill_route": (ctypes.c_int, [SP, RP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
         "uocr_ngram_ban": (ctypes.c_int, [_I32, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _I32,
                                           _P]),
-        "uocr_rope_page2d": (ctypes.c_int, [SP, _P, _I32, _P, _P, _I32, ctypes.c_float, _P]),
+        "uocr_rope_page2d": (ctypes.c_int, [SP, _P, _P, _I32, _P, _P, _I32, ctypes.c_float, _P]),
         "uocr_srswa_splits": (_I32, [SP, RP, _I32]),
         "uocr_srswa_decode": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
         "uocr_rswa_step": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P]),
@@ -300,16 +300,18 @@ def uocr_ngram_ban(tokens, n_gen, page_tokens, logits, ngram: int, window: int, 
           page_token, eos_token, max_page_tokens, _ptr(logits), V, dt, _stream(stream))
 
 
-def uocr_rope_page2d(shape: Shape, x, page, offset, page_mod: int = 2, base: float = 10000.0, stream=None) -> None:
-    """x [B][H][T][D] in shape's dtype, rotated in place; page, offset [B][T]
-    int32: the position of each token, shared by its heads."""
+def uocr_rope_page2d(shape: Shape, x, page, offset, page_mod: int = 2, base: float = 10000.0, y=None,
+                     stream=None) -> None:
+    """x (and y, if given) [B][H][T][D] in shape's dtype, rotated in place;
+    page, offset [B][T] int32: the position of each token, shared by its heads."""
     B, H, D, dt = shape.batch, shape.heads, shape.head_dim, shape.torch_dtype
     T = int(x.shape[2]) if x.dim() == 4 else -1
     _check(x, "x", dt, (B, H, T, D))
+    _check(y, "y", dt, (B, H, T, D), optional=True)
     _check(page, "page", torch.int32, (B, T))
     _check(offset, "offset", torch.int32, (B, T))
-    _call("uocr_rope_page2d", ctypes.byref(shape.c()), _ptr(x), T, _ptr(page), _ptr(offset), page_mod, base,
-          _stream(stream))
+    _call("uocr_rope_page2d", ctypes.byref(shape.c()), _ptr(x), _ptr(y), T, _ptr(page), _ptr(offset), page_mod,
+          base, _stream(stream))
 
 
 def uocr_srswa_decode(shape: Shape, route: Route, q, k_prefix, v_prefix, prefix_len, sel_idx, sel_bias,

@@ -141,8 +141,8 @@ def test_rope_page2d_validation():
     U, lib = _lib()
     sh = _shape(U)
 
-    def call(sh=sh, x=FAKE, tokens=64, page=FAKE, offset=FAKE, page_mod=2, base=10000.0):
-        return lib.uocr_rope_page2d(ctypes.byref(sh), x, tokens, page, offset, page_mod, base, None)
+    def call(sh=sh, x=FAKE, y=None, tokens=64, page=FAKE, offset=FAKE, page_mod=2, base=10000.0):
+        return lib.uocr_rope_page2d(ctypes.byref(sh), x, y, tokens, page, offset, page_mod, base, None)
 
     assert call(tokens=-1) == -2
     assert call(tokens=(1 << 20) + 1) == -2
@@ -154,11 +154,13 @@ def test_rope_page2d_validation():
     assert call(page=None) == -1
     assert call(offset=None) == -1
     assert call(x=ODD) == -5                    # rows are read as 16-byte chunks
+    assert call(y=ODD) == -5
+    assert call(y=FAKE) == -2                   # y is x
     assert call(page=ctypes.c_void_p(0x10002)) == -5
     assert call(sh=_shape(U, head_dim=96)) == -6
     assert call(sh=_shape(U, dtype=3)) == -3
     assert call(tokens=0, x=None, page=None, offset=None) == 0   # nothing to do
-    assert lib.uocr_rope_page2d(None, FAKE, 4, FAKE, FAKE, 2, 10000.0, None) == -1
+    assert lib.uocr_rope_page2d(None, FAKE, None, 4, FAKE, FAKE, 2, 10000.0, None) == -1
 
 
 def test_split_geometry():

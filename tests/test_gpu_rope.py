@@ -89,6 +89,29 @@ def test_rope_other_base_and_decode_shape():
     _check(got, want, "bf16", "decode step, base 5e5")
 
 
+@pytest.mark.parametrize("T", [1, 37])
+def test_rope_queries_and_keys_in_one_launch(T):
+    """x = queries, y = keys: both turned by the same positions, each exactly
+    as a call of its own would turn it."""
+    need_gpu()
+    B, H, D = 4, 3, 128
+    say("rope q+k", B, H, T, D)
+    q = S.rope_rows(21, B, H, T, D, "bf16")
+    k = S.rope_rows(22, B, H, T, D, "bf16")
+    page, offset = S.page_positions(4, B, T, 64, first_page=1, start_offset=30)
+    shape = U.Shape(B, H, D, 0, dtype=U.UOCR_BF16)
+    tq, tk = to_device(q, "bf16"), to_device(k, "bf16")
+    tp, to = torch.from_numpy(page).cuda(), torch.from_numpy(offset).cuda()
+    U.uocr_rope_page2d(shape, tq, tp, to, y=tk)
+    tk2 = to_device(k, "bf16")
+    U.uocr_rope_page2d(shape, tk2, tp, to)
+    torch.cuda.synchronize()
+    assert torch.equal(tk, tk2)
+    for name, src, t in [("q", q, tq), ("k", k, tk)]:
+        want = _oracle(S.widen(src, "bf16"), page, offset, 2, 10000.0)
+        _check(to_host(t), want, "bf16", f"{name} T={T}")
+
+
 def test_rope_negative_positions_count_as_zero_and_empty_is_a_no_op():
     need_gpu()
     B, H, T, D = 2, 2, 20, 64
