@@ -133,6 +133,38 @@ def test_entmax_topk_ties_resolved_by_index():
     np.testing.assert_allclose(prob.cpu().numpy()[1, 1], 1.0 / nb, rtol=1e-6)
 
 
+@pytest.mark.parametrize("nb", [50, 100, 200, 400, 1000])
+def test_entmax_topk_one_wave_ties_and_signed_zeros(nb):
+    """The one-wave path (a small candidate set) with exact ties across the
+    rank-k boundary, and with +0 and -0 scores, which the float order takes as
+    equal: the selection must follow (score desc, index asc) bit for bit."""
+    need_gpu()
+    say("one-wave ties", nb)
+    B, H, k = 2, 2, 16
+    rng = np.random.default_rng(nb)
+    sc = (rng.standard_normal((B, H, nb)) - 30.0).astype(np.float32)
+    for h in range(H):
+        top = rng.permutation(nb)[:22]
+        sc[0, h, top[:10]] = 3.0          # ranks 0-9
+        sc[0, h, top[10:]] = 2.75         # 12 equal scores across rank 16
+        zeros = rng.permutation(nb)[:20]
+        sc[1, h, zeros[:10]] = 0.0
+        sc[1, h, zeros[10:]] = -0.0       # 20 zeros of both signs: the top 16 by index
+        sc[1, h, rng.permutation(np.setdiff1d(np.arange(nb), zeros))[:5]] = -0.5
+    shape, route = U.Shape(B, H, 128, nb * 32), U.Route(topk=k)
+    idx = torch.empty((B, H, k), dtype=torch.int32, device="cuda")
+    prob = torch.empty((B, H, k), dtype=torch.float32, device="cuda")
+    bias = torch.empty((B, H, k), dtype=torch.float32, device="cuda")
+    U.uocr_entmax15_topk(shape, route, torch.from_numpy(sc).cuda(),
+                         torch.full((B,), nb * 32, dtype=torch.int32, device="cuda"), idx, prob, bias)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            assert _check_selection(idx.cpu().numpy()[b, h], prob.cpu().numpy()[b, h].astype(float),
+                                    bias.cpu().numpy()[b, h].astype(float), sc[b, h].astype(float), k,
+                                    what=f"nb={nb} b={b} h={h}")
+
+
 @pytest.mark.parametrize("live,with_bias", [(0, True), (1, True), (5, True), (16, True), (16, False)])
 def test_srswa_decode_given_selection(live, with_bias):
     """Sparse decode on its own, for a given routing result: every live
