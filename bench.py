@@ -246,7 +246,24 @@ def prefill_main(args):
     flops = w.units * (2.0 * w.idx_dim * visible + 2.0 * w.head_dim * w.idx_dim * tq)
     achieved = flops / (ms * 1e-3) / 1e12
     hbm = w.units * (tq * w.head_dim * w.elem_bytes + nb * w.idx_dim * 4 + tq * w.topk * 12)
-    idx = outs[(K - 1) % len(sessions)][0]
+    # the chunk's block-key update: blocks from the one holding the chunk's first
+    # token to the end of the prefix (uocr_block_index_range), against a full build
+    first, last = q_pos // w.block, nb
+    iu = []
+    for fn in ("range", "full"):
+        for i in range(3):
+            s = sessions[i % len(sessions)]
+            (U.uocr_block_index_range(s.shape, s.route, s.k_prefix, s.prefix_len, s.proj, s.kbar, first, last)
+             if fn == "range" else s.build_index())
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(K):
+            s = sessions[i % len(sessions)]
+            (U.uocr_block_index_range(s.shape, s.route, s.k_prefix, s.prefix_len, s.proj, s.kbar, first, last)
+             if fn == "range" else s.build_index())
+        e1.record()
+        torch.cuda.synchronize()
+        iu.append(round(e0.elapsed_time(e1) / K * 1e3, 2))
     result = {
         "metric": "prefill routing queries/s (batch x heads x chunk tokens)", "value": round(queries / (ms * 1e-3), 1),
         "unit": "queries/s", "n_gpus": 1, "steps": K, "warmup": max(args.warmup // 20, 3),
@@ -260,6 +277,7 @@ def prefill_main(args):
                      "traffic": None},
         "flops_per_launch": flops, "hbm_bytes_per_launch": hbm,
         "hbm_gbs": round(hbm / (ms * 1e-3) / 1e9, 1),
+        "index_update": {"blocks": [first, last], "range_us": iu[0], "full_build_us": iu[1]},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = prefill_cpu_baseline(w, min(tq, 256), q_pos, args.cpu_seconds)

@@ -151,6 +151,20 @@ int uocr_block_index_build(const uocr_shape* shape, const uocr_route* route,
                            const void* k_prefix, const int32_t* prefix_len,
                            const float* proj, float* kbar_idx, void* stream);
 
+/* uocr_block_index_range -- the same, for blocks [first_block, last_block) of
+ * every unit only; rows outside the range are left as they are.  For a
+ * prefix that grows by chunks (chunked prefill): after the tokens
+ * [m_old, m_new) are written, a call with prefix_len = m_new and the range
+ * [floor(m_old/32), ceil(m_new/32)) brings kbar_idx to what a full build at
+ * m_new gives, bit for bit, reading only the new tokens and the partial
+ * block before them.  0 <= first_block <= last_block <= nb_cap (else
+ * UOCR_ERR_SHAPE); an empty range does nothing.                             */
+int uocr_block_index_range(const uocr_shape* shape, const uocr_route* route,
+                           const void* k_prefix, const int32_t* prefix_len,
+                           const float* proj, float* kbar_idx,
+                           int32_t first_block, int32_t last_block,
+                           void* stream);
+
 /* ---------------------------------------------------------------------------
  * uocr_block_score -- relevance of every prefix block to the query.
  * [nxmr.cn/news/162408 "稀疏路由" step 2.]

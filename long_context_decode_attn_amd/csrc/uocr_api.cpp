@@ -158,6 +158,29 @@ int srswa_waves(const uocr_route* r, int32_t req) {
   return W;
 }
 
+int block_index(const char* fn, const uocr_shape* shape, const uocr_route* route, const void* k_prefix,
+                const int32_t* prefix_len, const float* proj, float* kbar_idx, int32_t first_block,
+                int32_t last_block, void* stream) {
+  CHECK(check_shape(shape, fn));
+  CHECK(check_route(shape, route, fn));
+  NEED(prefix_len, "prefix_len");
+  NEED(proj, "proj");
+  ALIGN4(prefix_len, "prefix_len");
+  ALIGN16(proj, "proj");
+  const int nb_cap = nb_cap_of(shape);
+  if (first_block < 0 || last_block < first_block || last_block > nb_cap)
+    return fail(UOCR_ERR_SHAPE, "%s: block range [%d, %d) outside [0, %d]", fn, first_block, last_block, nb_cap);
+  if (first_block == last_block) return ok();
+  NEED(k_prefix, "k_prefix");
+  NEED(kbar_idx, "kbar_idx");
+  ALIGN16(k_prefix, "k_prefix");
+  ALIGN16(kbar_idx, "kbar_idx");
+  uocr::IndexArgs a{k_prefix, prefix_len, proj,        kbar_idx,    units_of(shape),
+                    shape->heads, shape->prefix_cap, nb_cap, first_block, last_block - first_block};
+  return hip_status(uocr::launch_block_index(shape->dtype, shape->head_dim, a,
+                                             static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -277,22 +300,18 @@ int uocr_block_index_build(const uocr_shape* shape, const uocr_route* route, con
                            const int32_t* prefix_len, const float* proj, float* kbar_idx,
                            void* stream) {
   const char* fn = "uocr_block_index_build";
-  CHECK(check_shape(shape, fn));
-  CHECK(check_route(shape, route, fn));
-  NEED(prefix_len, "prefix_len");
-  NEED(proj, "proj");
-  ALIGN4(prefix_len, "prefix_len");
-  ALIGN16(proj, "proj");
-  if (shape->prefix_cap == 0) return ok();
-  NEED(k_prefix, "k_prefix");
-  NEED(kbar_idx, "kbar_idx");
-  ALIGN16(k_prefix, "k_prefix");
-  ALIGN16(kbar_idx, "kbar_idx");
-  uocr::IndexArgs a{k_prefix, prefix_len, proj, kbar_idx, units_of(shape), shape->heads,
-                    shape->prefix_cap, nb_cap_of(shape)};
-  return hip_status(uocr::launch_block_index(shape->dtype, shape->head_dim, a,
-                                             static_cast<hipStream_t>(stream)), fn);
+  if (shape == nullptr) return fail(UOCR_ERR_NULL, "%s: shape is NULL", fn);
+  return block_index(fn, shape, route, k_prefix, prefix_len, proj, kbar_idx, 0, nb_cap_of(shape), stream);
 }
+
+int uocr_block_index_range(const uocr_shape* shape, const uocr_route* route, const void* k_prefix,
+                           const int32_t* prefix_len, const float* proj, float* kbar_idx,
+                           int32_t first_block, int32_t last_block, void* stream) {
+  return block_index("uocr_block_index_range", shape, route, k_prefix, prefix_len, proj, kbar_idx,
+                     first_block, last_block, stream);
+}
+
+
 
 int uocr_block_score(const uocr_shape* shape, const uocr_route* route, const void* q,
                      const float* proj, const float* kbar_idx, const int32_t* prefix_len,

@@ -45,6 +45,7 @@ struct IndexArgs {
   const float* proj;
   float* kbar;
   int units, heads, prefix_cap, nb_cap;
+  int first_block, n_blocks;  // blocks [first_block, first_block + n_blocks) of every unit
 };
 
 struct ScoreArgs {

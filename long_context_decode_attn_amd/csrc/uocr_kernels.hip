@@ -706,7 +706,7 @@ __global__ __launch_bounds__(256) void k_block_index(IndexArgs a) {
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int grp = lane / G::LPR, c = lane % G::LPR;
-  const long long total = (long long)a.units * a.nb_cap;
+  const long long total = (long long)a.units * a.n_blocks;  // items (unit, block in range)
   const long long nw = (long long)gridDim.x * kWaves;
   const long long per = (total + nw - 1) / nw;
   const long long beg = ((long long)blockIdx.x * kWaves + (threadIdx.x >> 6)) * per;
@@ -724,23 +724,24 @@ __global__ __launch_bounds__(256) void k_block_index(IndexArgs a) {
     }
   };
 
-  int unit = (int)(beg / a.nb_cap), j = (int)(beg - (long long)unit * a.nb_cap);
+  const int jend = a.first_block + a.n_blocks;
+  int unit = (int)(beg / a.n_blocks), j = a.first_block + (int)(beg - (long long)unit * a.n_blocks);
   int m = limit(unit);
   int nr = min(kBlock, m - j * kBlock);  // rows of the block inside the prefix (<= 0: none)
   uint4 kv[NR];
   load(kv, unit, j, nr);
   for (long long item = beg; item < end; ++item) {
     int nunit = unit, nj = j + 1, nm = m;
-    if (nj == a.nb_cap) {
+    if (nj == jend) {
       ++nunit;
-      nj = 0;
+      nj = a.first_block;
       nm = item + 1 < end ? limit(nunit) : 0;
     }
     const int nnr = item + 1 < end ? min(kBlock, nm - nj * kBlock) : 0;
     uint4 kn[NR];
     load(kn, nunit, nj, nnr);
 
-    float* dst = a.kbar + item * kIdxDim;
+    float* dst = a.kbar + ((size_t)unit * a.nb_cap + j) * kIdxDim;
     if (nr <= 0) {
       if (lane < kIdxDim) dst[lane] = 0.f;
     } else {
@@ -2276,7 +2277,7 @@ hipError_t launch_block_index_t(const IndexArgs& a, size_t items, hipStream_t s)
 }
 
 hipError_t launch_block_index(int dtype, int head_dim, const IndexArgs& a, hipStream_t s) {
-  const size_t items = (size_t)a.units * a.nb_cap;
+  const size_t items = (size_t)a.units * a.n_blocks;
   if (items == 0) return hipSuccess;
   if (dtype == 0 && head_dim == 64) return launch_block_index_t<0, 64>(a, items, s);
   if (dtype == 0 && head_dim == 128) return launch_block_index_t<0, 128>(a, items, s);

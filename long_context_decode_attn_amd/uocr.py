@@ -113,6 +113,7 @@ def load_library():
         "uocr_rswa_workspace_bytes": (_SZ, [SP, _I32]),
         "uocr_rswa_decode": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P]),
         "uocr_block_index_build": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P]),
+        "uocr_block_index_range": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _I32, _I32, _P]),
         "uocr_block_score": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P]),
         "uocr_entmax15_topk": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P]),
         "uocr_prefill_route": (ctypes.c_int, [SP, RP, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -137,7 +138,7 @@ def load_library():
 
 
 EXPORTED = ("uocr_ring_append", "uocr_rswa_splits", "uocr_rswa_workspace_bytes",
-            "uocr_rswa_decode", "uocr_block_index_build", "uocr_block_score", "uocr_entmax15_topk",
+            "uocr_rswa_decode", "uocr_block_index_build", "uocr_block_index_range", "uocr_block_score", "uocr_entmax15_topk",
             "uocr_prefill_route", "uocr_ngram_ban", "uocr_rope_page2d",
             "uocr_srswa_splits", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
             "uocr_status_string", "uocr_last_error", "uocr_version")
@@ -241,6 +242,17 @@ def uocr_block_index_build(shape: Shape, route: Route, k_prefix, prefix_len, pro
     _check(kbar_idx, "kbar_idx", torch.float32, (B, H, shape.nb_cap, route.idx_dim))
     _call("uocr_block_index_build", ctypes.byref(shape.c()), ctypes.byref(route.c()), _ptr(k_prefix),
           _ptr(prefix_len), _ptr(proj), _ptr(kbar_idx), _stream(stream))
+
+
+def uocr_block_index_range(shape: Shape, route: Route, k_prefix, prefix_len, proj, kbar_idx, first_block: int,
+                           last_block: int, stream=None) -> None:
+    B, H, D, m, dt = shape.batch, shape.heads, shape.head_dim, shape.prefix_cap, shape.torch_dtype
+    _check(k_prefix, "k_prefix", dt, (B, H, m, D))
+    _check(prefix_len, "prefix_len", torch.int32, (B,))
+    _check(proj, "proj", torch.float32, (D, route.idx_dim))
+    _check(kbar_idx, "kbar_idx", torch.float32, (B, H, shape.nb_cap, route.idx_dim))
+    _call("uocr_block_index_range", ctypes.byref(shape.c()), ctypes.byref(route.c()), _ptr(k_prefix),
+          _ptr(prefix_len), _ptr(proj), _ptr(kbar_idx), first_block, last_block, _stream(stream))
 
 
 def uocr_block_score(shape: Shape, route: Route, q, proj, kbar_idx, prefix_len, scores, stream=None) -> None:

@@ -137,6 +137,22 @@ def test_ngram_ban_validation():
     assert call(batch=0, tokens=None, n_gen=None, logits=None) == 0
 
 
+def test_block_index_range_validation():
+    U, lib = _lib()
+    sh, r = _shape(U), U._Route(32, 32, 16)          # prefix_cap 320: nb_cap 10
+
+    def call(first, last, k=FAKE, kbar=FAKE):
+        return lib.uocr_block_index_range(ctypes.byref(sh), ctypes.byref(r), k, FAKE, FAKE, kbar, first, last, None)
+
+    assert call(-1, 4) == -2
+    assert call(5, 4) == -2
+    assert call(0, 11) == -2
+    assert call(3, 3, k=None, kbar=None) == 0      # empty range: nothing to do
+    assert call(0, 10, k=None) == -1
+    assert call(2, 7, kbar=ODD) == -5
+    assert lib.uocr_block_index_range(None, ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, 0, 1, None) == -1
+
+
 def test_rope_page2d_validation():
     U, lib = _lib()
     sh = _shape(U)

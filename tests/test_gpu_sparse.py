@@ -133,6 +133,35 @@ def test_entmax_topk_ties_resolved_by_index():
     np.testing.assert_allclose(prob.cpu().numpy()[1, 1], 1.0 / nb, rtol=1e-6)
 
 
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("f32", 64)])
+def test_block_index_range_grows_with_the_prefix(dtype, head_dim):
+    """Chunked prefill: after each chunk, rebuilding only the blocks from the
+    one holding the old end gives, bit for bit, what a full build at the new
+    lengths gives (per-sequence lengths differ; blocks past a sequence's
+    prefix are zero in both)."""
+    need_gpu()
+    w = _small_sparse(batch=3, heads=2, pages=6, prompt=0, dtype=dtype, head_dim=head_dim)
+    say("index range", dtype, head_dim)
+    kv = S.prefix_kv(w)
+    sess = DecodeSession(w, prefix_kv=kv)
+    full = DecodeSession(w, prefix_kv=kv)
+    sess.kbar.zero_()
+    old = np.zeros(w.batch, dtype=np.int64)
+    for step, base in enumerate([70, 700, 701, 1100, w.prefix_len]):
+        new = np.minimum(base + 37 * np.arange(w.batch), w.prefix_len)
+        first = int(old.min()) // 32
+        last = -(-int(new.max()) // 32)
+        pl = torch.from_numpy(new.astype(np.int32)).cuda()
+        sess.prefix_len.copy_(pl)
+        U.uocr_block_index_range(sess.shape, sess.route, sess.k_prefix, sess.prefix_len, sess.proj, sess.kbar,
+                                 first, last)
+        full.prefix_len.copy_(pl)
+        full.build_index()
+        torch.cuda.synchronize()
+        assert torch.equal(sess.kbar, full.kbar), f"chunk {step}: range [{first}, {last})"
+        old = new
+
+
 @pytest.mark.parametrize("nb", [50, 100, 200, 400, 1000])
 def test_entmax_topk_one_wave_ties_and_signed_zeros(nb):
     """The one-wave path (a small candidate set) with exact ties across the
