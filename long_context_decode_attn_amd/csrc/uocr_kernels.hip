@@ -1563,6 +1563,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kPrefillThreads = 512;
 constexpr int kPrefillScores = 12288;  // LDS score slots: qt x nb_cap
+constexpr int kPrefillTilesInFlight = 1;  // key tiles per wave with loads in flight (4 measured slower)
 constexpr int kPrefillMaxQ = 16;
 constexpr int32_t kDeferred = INT32_MIN;
 
@@ -1574,13 +1575,26 @@ struct PrefillSmem {
 };
 
 // Query i of the tile starting at chunk query q0: position and visible blocks.
+// Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i mod 8),
+// and each XCD has its own L2.  The workgroups of one unit all read that
+// unit's block keys, so this permutation gives XCD x a contiguous range of
+// the logical workgroups, i.e. of the units: each unit's keys then sit in
+// one L2 instead of eight.  Any order is correct; this one only keeps reuse
+// inside an L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+  const int q = n / kXcds, r = n % kXcds, x = b % kXcds;
+  return x * q + min(x, r) + b / kXcds;
+}
+
 struct PrefillTile {
   int unit, q0, nq, m, nb_all;
   long long pos0;
   __device__ PrefillTile(const PrefillArgs& a) {
     const int tiles = (a.tq + a.qt - 1) / a.qt;
-    unit = blockIdx.x / tiles;
-    q0 = (blockIdx.x - unit * tiles) * a.qt;
+    const int wg = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
+    unit = wg / tiles;
+    q0 = (wg - unit * tiles) * a.qt;
     nq = min(a.qt, a.tq - q0);
     const int b = unit / a.heads;
     m = min(max(a.prefix_len[b], 0), a.prefix_cap);
@@ -1625,45 +1639,55 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
   const PrefillTile t(a);
   const int nbmax = t.visible(t.nq - 1);
 
-  // 1. q_idx: P and the tile's queries are staged in the (not yet used)
-  //    score buffer with coalesced loads, then one thread per (query, dim)
+  typedef double v4d __attribute__((ext_vector_type(4)));
+  const int lr = lane % 16, lk = lane / 16;
+  const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
+  const int ntiles = (nbmax + 15) / 16;
+  auto load_b = [&](float4 (&bf)[2], int tile) {  // this lane's dims of one key of a tile
+    const int j = tile * 16 + lr;
+    const bool jok = j < nbmax;
+    const float4* kr = reinterpret_cast<const float4*>(K + (size_t)(jok ? j : 0) * kIdxDim) + lk;
+    bf[0] = jok ? kr[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+    bf[1] = jok ? kr[4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  // this wave's first kPrefillTilesInFlight key tiles do not depend on q_idx:
+  // their loads go first, and each tile consumed below puts the loads of the
+  // tile that many steps later in flight
+  float4 bq[kPrefillTilesInFlight][2];
+#pragma unroll
+  for (int u = 0; u < kPrefillTilesInFlight; ++u)
+    if (wave + u * W < ntiles) load_b(bq[u], wave + u * W);
+
+  // 1. q_idx on the matrix cores, fp64, with the operands read straight from
+  //    global memory (P [D][32] is shared by every workgroup and stays in L2):
+  //    wave w computes the 16 x 16 tile of columns 16 (w % 2) .. + 15 over the
+  //    quarter w / 2 of the D terms, in the operand layout of the scores
+  //    below; the four quarters are summed in a fixed order through LDS
   {
-    float* Ps = sm.scores;                 // [D][32]
-    float* Qs = sm.scores + D * kIdxDim;   // [nq][D]
-    for (int e = tid; e < D * kIdxDim; e += kPrefillThreads) Ps[e] = a.proj[e];
-    const char* q0 = static_cast<const char*>(a.q) + ((size_t)t.unit * a.tq + t.q0) * Geo<DT, D>::ROWB;
-    for (int e = tid; e < t.nq * D; e += kPrefillThreads) {
-      if constexpr (DT == 0)
-        Qs[e] = reinterpret_cast<const float*>(q0)[e];
-      else
-        Qs[e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(q0)[e] << 16);
-    }
-    __syncthreads();
-    // on the matrix cores, fp64: wave w computes the 16 x 16 tile of
-    // columns 16 (w % 2) .. + 15 over the quarter w / 2 of the D terms (same
-    // operand layout as the scores below); the four quarters are summed in a
-    // fixed order through LDS
-    typedef double v4d __attribute__((ext_vector_type(4)));
     static_assert(kPrefillThreads == 512 && kIdxDim == 32 && kPrefillMaxQ <= 16, "q_idx tiling");
-    double* part = reinterpret_cast<double*>(sm.scores + D * kIdxDim + kPrefillMaxQ * D);  // [4][16][32]
-    {
-      const int lr = lane % 16, lk = lane / 16, c0 = 16 * (wave & 1), k0 = (wave >> 1) * (D / 4);
-      v4d acc = {0.0, 0.0, 0.0, 0.0};
+    double* part = reinterpret_cast<double*>(sm.scores);  // [4][16][32], before any score is written
+    const int c0 = 16 * (wave & 1), k0 = (wave >> 1) * (D / 4);
+    const char* qrow = static_cast<const char*>(a.q) +
+                       ((size_t)t.unit * a.tq + t.q0 + (lr < t.nq ? lr : 0)) * Geo<DT, D>::ROWB;
+    float qa[D / 16], pb[D / 16];
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const int dd = k0 + 4 * st + lk;
-        const double av = lr < t.nq ? (double)Qs[lr * D + dd] : 0.0;
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)Ps[dd * kIdxDim + c0 + lr], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part[((wave >> 1) * 16 + lk + 4 * r) * kIdxDim + c0 + lr] = acc[r];
+    for (int st = 0; st < D / 16; ++st) {
+      const int dd = k0 + 4 * st + lk;
+      if constexpr (DT == 0)
+        qa[st] = reinterpret_cast<const float*>(qrow)[dd];
+      else
+        qa[st] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[dd] << 16);
+      pb[st] = a.proj[dd * kIdxDim + c0 + lr];
     }
+    v4d acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(lr < t.nq ? (double)qa[st] : 0.0, (double)pb[st], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[((wave >> 1) * 16 + lk + 4 * r) * kIdxDim + c0 + lr] = acc[r];
     __syncthreads();
-    {
-      const int qi = tid / kIdxDim, i = tid % kIdxDim;
-      if (qi < t.nq)
-        sm.qidx[qi][i] = ((part[tid] + part[512 + tid]) + part[1024 + tid]) + part[1536 + tid];
-    }
+    const int qi = tid / kIdxDim, i = tid % kIdxDim;
+    if (qi < t.nq) sm.qidx[qi][i] = ((part[tid] + part[512 + tid]) + part[1024 + tid]) + part[1536 + tid];
   }
   __syncthreads();
 
@@ -1676,8 +1700,6 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
   //    sum, so lane group g takes dims 4g .. 4g+3 at steps 0-3 and 16+4g ..
   //    16+4g+3 at steps 4-7: its key values are two 16-byte loads per tile.
   {
-    typedef double v4d __attribute__((ext_vector_type(4)));
-    const int lr = lane % 16, lk = lane / 16;
     double af[kIdxDim / 4];
 #pragma unroll
     for (int st = 0; st < kIdxDim / 4; ++st)
@@ -1685,29 +1707,24 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
     int vis[4];  // blocks visible to the queries of this lane's result rows
 #pragma unroll
     for (int r = 0; r < 4; ++r) vis[r] = lk + 4 * r < t.nq ? t.visible(lk + 4 * r) : 0;
-    const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
-    const int ntiles = (nbmax + 15) / 16;
-    auto load_b = [&](float4 (&bf)[2], int tile) {  // this lane's dims of one key of a tile
-      const int j = tile * 16 + lr;
-      const bool jok = j < nbmax;
-      const float4* kr = reinterpret_cast<const float4*>(K + (size_t)(jok ? j : 0) * kIdxDim) + lk;
-      bf[0] = jok ? kr[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-      bf[1] = jok ? kr[4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    };
-    float4 bn[2];
-    if (wave < ntiles) load_b(bn, wave);
-    for (int tile = wave; tile < ntiles; tile += W) {
-      const int j = tile * 16 + lr;
-      const float4 b0 = bn[0], b1 = bn[1];
-      if (tile + W < ntiles) load_b(bn, tile + W);  // next tile's keys in flight meanwhile
-      const float bf[kIdxDim / 4] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      v4d acc = {0.0, 0.0, 0.0, 0.0};
+    constexpr int NF = kPrefillTilesInFlight;
+    for (int t0 = wave; t0 < ntiles; t0 += NF * W) {
 #pragma unroll
-      for (int st = 0; st < kIdxDim / 4; ++st)
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[st], (double)bf[st], acc, 0, 0, 0);
+      for (int u = 0; u < NF; ++u) {
+        const int tile = t0 + u * W;
+        if (tile >= ntiles) break;
+        const int j = tile * 16 + lr;
+        const float4 b0 = bq[u][0], b1 = bq[u][1];
+        if (tile + NF * W < ntiles) load_b(bq[u], tile + NF * W);
+        const float bf[kIdxDim / 4] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        v4d acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (j < vis[r]) sm.scores[(lk + 4 * r) * a.nb_cap + j] = (float)acc[r];
+        for (int st = 0; st < kIdxDim / 4; ++st)
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(af[st], (double)bf[st], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j < vis[r]) sm.scores[(lk + 4 * r) * a.nb_cap + j] = (float)acc[r];
+      }
     }
   }
   if (tid == 0) sm.next_q = W;  // queries past the first W go to whichever wave is free
