@@ -39,13 +39,13 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("a713ec93c82712cf", 45138034, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("a713ec93c82712cf", 18835927, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("a713ec93c82712cf", 892115251, 1024662),
-    ("uocr_rswa_step", "dense-1p-b512"): ("a713ec93c82712cf", 1092083446, 3940443),
-    ("uocr_rswa_step", "dense-40p-b32"): ("a713ec93c82712cf", 1699311085, 686692),
-    ("uocr_rswa_step", "dense-125p-b8"): ("a713ec93c82712cf", 1316296546, 302160),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("a713ec93c82712cf", 169070021, 167798318),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("49cd24f57481bc32", 45138100, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("49cd24f57481bc32", 18836139, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("49cd24f57481bc32", 892115184, 1024654),
+    ("uocr_rswa_step", "dense-1p-b512"): ("49cd24f57481bc32", 1092083486, 3940450),
+    ("uocr_rswa_step", "dense-40p-b32"): ("49cd24f57481bc32", 1699311028, 686686),
+    ("uocr_rswa_step", "dense-125p-b8"): ("49cd24f57481bc32", 1316296841, 302159),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("49cd24f57481bc32", 169110038, 167805805),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
