@@ -1,0 +1,48 @@
+"""bench.py on the host: the refusal of more than one GPU, and the byte model
+behind its roofline against the per-unit figures of the measurement plan
+(bytes each step must move at the pages' shapes: bf16, D = 128, n = 128)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from long_context_decode_attn_amd import synth as S  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+# bytes per unit per step: append 1,024 B; dense decode q + 2 (m + w) D 2 + out;
+# sparse decode q + selection + 2 (512 + w) D 2 + out = 328,320 B
+@pytest.mark.parametrize("name,per_unit,kernel", [
+    ("dense-10p-b64", 1_394_176, None),            # 2720 tokens per unit
+    ("dense-1p-b512", 214_528, None),              # 416 tokens
+    ("dense-40p-b32", 5_309_952, None),            # 10368 tokens
+    ("dense-125p-b8", 16_451_072, None),           # 32128 tokens
+    ("srswa-40p-b32", 328_320, "uocr_srswa_decode"),
+    ("srswa-125p-b8", 328_320, "uocr_srswa_decode"),
+])
+def test_algorithmic_bytes_follow_the_per_unit_figures(name, per_unit, kernel):
+    w = S.WORKLOADS[name]
+    b = bench.algorithmic_bytes(w)   # every selected block counted (the nominal figure)
+    got = b[kernel] if kernel else b["uocr_ring_append"] + b["uocr_rswa_decode"]
+    assert abs(got / w.units - per_unit) <= 2.0, (name, got / w.units, per_unit)
+
+
+def test_sparse_full_step_bytes():
+    """Full SR-SWA step at 40 pages: 372,992 B per unit (119.4 MB per step),
+    within the accounting of the score round trip (nb x 4 B written, then read)."""
+    w = S.WORKLOADS["srswa-40p-b32"]
+    b = bench.algorithmic_bytes(w)
+    step = sum(b.values())
+    assert abs(step / w.units - 372_992) / 372_992 < 2e-3
+    assert abs(step / 1e6 - 119.4) < 0.3
