@@ -138,10 +138,6 @@ __device__ __forceinline__ float sum16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float sum32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 __device__ __forceinline__ double join(unsigned lo, unsigned hi) {
   return __longlong_as_double(((long long)hi << 32) | lo);
 }
@@ -201,18 +197,6 @@ __device__ __forceinline__ int wave_count_below(const float (&v)[NS], float T) {
 #pragma unroll
   for (int e = 0; e < NS; ++e) c += __popcll(__ballot(v[e] < T));
   return c;
-}
-
-// Exclusive prefix over the lanes of a wave of a small non-negative count
-// (< 32), from one ballot per bit: no LDS round trip.
-__device__ __forceinline__ int wave_prefix_small(int c) {
-  int base = 0;
-#pragma unroll
-  for (int bit = 0; bit < 5; ++bit) {
-    const uint64_t m = __ballot((c >> bit) & 1);
-    base += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << bit;
-  }
-  return base;
 }
 
 __device__ __forceinline__ float readlane_f(float x, int lane) {

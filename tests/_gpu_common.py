@@ -1,7 +1,6 @@
 """Shared helpers of the GPU parity tests (not collected as tests)."""
 from __future__ import annotations
 
-import math
 import sys
 
 import numpy as np
@@ -10,7 +9,6 @@ import torch
 
 from long_context_decode_attn_amd import synth as S
 from long_context_decode_attn_amd import uocr as U
-from long_context_decode_attn_amd.session import DecodeSession, to_device, to_host
 from oracle import uocr_oracle as O
 
 BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 1e-2

@@ -5,7 +5,6 @@ import pytest
 import torch
 
 from long_context_decode_attn_amd import synth as S
-from long_context_decode_attn_amd import uocr as U
 from long_context_decode_attn_amd.session import DecodeSession, to_device, to_host
 from oracle import uocr_oracle as O
 from tests._gpu_common import HostMirror, assert_close, need_gpu, say

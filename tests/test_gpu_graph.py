@@ -1,6 +1,5 @@
 """Decode steps captured in a HIP graph: every replay matches the same steps
 run eagerly, with eager work and synchronisations between the replays."""
-import numpy as np
 import pytest
 import torch
 

@@ -7,11 +7,9 @@ show that the check catches the mistake.  No GPU is used here.
 import heapq
 import math
 import os
-from collections import deque
 from fractions import Fraction
 
 import numpy as np
-import pytest
 import torch
 
 from oracle import uocr_oracle as O
