@@ -39,13 +39,13 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("49cd24f57481bc32", 45138100, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("49cd24f57481bc32", 18836139, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("49cd24f57481bc32", 892115184, 1024654),
-    ("uocr_rswa_step", "dense-1p-b512"): ("49cd24f57481bc32", 1092083486, 3940450),
-    ("uocr_rswa_step", "dense-40p-b32"): ("49cd24f57481bc32", 1699311028, 686686),
-    ("uocr_rswa_step", "dense-125p-b8"): ("49cd24f57481bc32", 1316296841, 302159),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("49cd24f57481bc32", 169110038, 167805805),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("c63d74cb602a3ad0", 45138123, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("c63d74cb602a3ad0", 18835928, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("c63d74cb602a3ad0", 892115157, 1024665),
+    ("uocr_rswa_step", "dense-1p-b512"): ("c63d74cb602a3ad0", 1092083624, 3940444),
+    ("uocr_rswa_step", "dense-40p-b32"): ("c63d74cb602a3ad0", 1699311165, 686684),
+    ("uocr_rswa_step", "dense-125p-b8"): ("c63d74cb602a3ad0", 1316296792, 302159),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("c63d74cb602a3ad0", 169109992, 167796425),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
