@@ -253,7 +253,8 @@ int uocr_ngram_ban(int32_t batch, const int32_t* tokens, int32_t ring_cap,
  * RoFormer's (Su et al., 2021).  The page gives neither the frequencies nor
  * the split of the head dimension: the choices below are this library's.]
  *   x       [B][H][tokens][D] in shape->dtype (queries or keys), rotated in
- *           place; only batch, heads, head_dim and dtype of shape are used;
+ *           place; batch, heads, head_dim and dtype of shape are used (its
+ *           other fields must still pass the checks every call makes);
  *   y       NULL, or a second tensor of the same layout turned by the same
  *           positions in the same launch (e.g. x = q, y = k_new of a decode
  *           step); it must not be x;
