@@ -260,6 +260,29 @@ def test_srswa_wide_support_and_ragged(fused):
     _run_sparse(w, steps=4, fused=fused, t_gen=[0, 9, 500], flat=True)
 
 
+# unusual shapes: head dims, dtypes, windows from 1 to 1024 slots, top-k from
+# 1 to 64, prefixes that end inside a block, counts before / across a wrap
+_SWEEP = [
+    dict(dtype="bf16", head_dim=64, window=8, topk=4, pages=2, prompt=5, t_gen=[0, 3, 20]),
+    dict(dtype="bf16", head_dim=128, window=200, topk=40, pages=3, prompt=31, t_gen=[0, 150, 1000]),
+    dict(dtype="f32", head_dim=128, window=64, topk=1, pages=1, prompt=0, t_gen=[64]),
+    dict(dtype="bf16", head_dim=128, window=128, topk=64, pages=9, prompt=7, t_gen=[127, 128, 129]),
+    dict(dtype="f32", head_dim=64, window=1, topk=16, pages=2, prompt=1, t_gen=[0, 1]),
+    dict(dtype="bf16", head_dim=64, window=1024, topk=16, pages=4, prompt=17, t_gen=[0, 700, 3000]),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("cfg", range(len(_SWEEP)))
+def test_srswa_shape_sweep(cfg, fused):
+    need_gpu()
+    c = dict(_SWEEP[cfg])
+    t_gen = c.pop("t_gen")
+    w = _small_sparse(batch=len(t_gen), heads=2, planted=3, t0=0, seed=200 + cfg, **c)
+    say("srswa sweep", cfg, c, t_gen, "fused" if fused else "")
+    _run_sparse(w, steps=3, fused=fused, t_gen=t_gen)
+
+
 def _run_sparse(w, steps, units=None, num_splits=0, k=None, fused=False, t_gen=None, flat=False):
     kv = S.prefix_kv(w)
     if flat:   # shrink the keys so that block scores are close together (wide support)
