@@ -103,6 +103,28 @@ def test_dense_bf16_ragged_prefix_and_window(num_splits, fused):
                num_splits=num_splits, fused=fused)
 
 
+# unusual shapes: windows from 1 to 1024 slots, per-sequence prefixes that end
+# inside a split or are empty, counts before / across a wrap, requested splits
+_DENSE_SWEEP = [
+    dict(dtype="bf16", D=64, window=1, prefix_len=[700, 0, 33], t_gen=[0, 1, 9], splits=0),
+    dict(dtype="bf16", D=128, window=8, prefix_len=[1, 1000], t_gen=[7, 8], splits=3),
+    dict(dtype="f32", D=128, window=200, prefix_len=[513, 512, 511], t_gen=[199, 200, 201], splits=0),
+    dict(dtype="bf16", D=64, window=1024, prefix_len=[64, 2000], t_gen=[3000, 100], splits=16),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("cfg", range(len(_DENSE_SWEEP)))
+def test_dense_shape_sweep(cfg, fused):
+    need_gpu()
+    c = dict(_DENSE_SWEEP[cfg])
+    pl, tg = c["prefix_len"], c["t_gen"]
+    w = S.Workload(f"dense-sweep-{cfg}", batch=len(pl), heads=2, head_dim=c["D"], dtype=c["dtype"], pages=8,
+                   prompt=0, t0=0, steps=3, seed=300 + cfg, window=c["window"])
+    say("dense sweep", cfg, c, "fused" if fused else "")
+    _run_dense(w, 3, prefix_cap=2048, prefix_len=pl, t_gen=tg, num_splits=c["splits"], fused=fused)
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 128), ("f32", 64)])
 def test_dense_other_dtypes_and_dims(dtype, D):
     need_gpu()
