@@ -954,14 +954,18 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
   // issue arbitration against the waves attending over the window
   __builtin_amdgcn_s_setprio(3);
   float sv[NS];
-  float lmax = -INFINITY;
+  float lmax = -INFINITY, lmin = INFINITY;
 #pragma unroll
   for (int e = 0; e < NS; ++e) {
     const int j = e * 64 + lane;
     sv[e] = j < nb ? s[j] : -INFINITY;
     lmax = fmaxf(lmax, sv[e]);
+    if constexpr (WIDE) lmin = j < nb ? fminf(lmin, sv[e]) : lmin;
   }
   const float smax = wave_max(lmax);
+  // WIDE: the largest gap smax - s of a visible block (the searches below
+  // start from it when the support is wide)
+  const float dlast = WIDE ? smax + wave_max(-lmin) : 0.f;
   const double dmax = (double)smax;
   float dv[NS];
 #pragma unroll
@@ -973,11 +977,20 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
     if (nA >= kk) break;
     T = T * 2.f;  // reaches +inf, where every finite d counts
   }
-  // Too many blocks below T for one wave: bisect T in (lo, hi) for a count in
-  // [kk, 64]; count(d < lo) < kk, except possibly at the first probe.
-  auto narrow = [&](float lo, float hi) -> bool {
+  // Too many blocks below T for one wave: search T in (lo, hi) for a count in
+  // [kk, 64], given count(d < hi) = chi > 64 and count(d < lo) < kk (except
+  // possibly at the first probe, which is lo itself).  Every other probe
+  // interpolates the count linearly between the ends, aiming at the middle
+  // of [kk, 64]; the others halve the interval, so the search takes at most
+  // about twice the probes of a bisection.
+  auto narrow = [&](float lo, float hi, int chi) -> bool {
+    int clo = -1;
     for (int it = 0; it < 48; ++it) {
-      const float mid = it == 0 ? lo : 0.5f * (lo + hi);
+      float mid = it == 0 ? lo : 0.5f * (lo + hi);
+      if ((it & 1) && clo >= 0) {
+        const float g = lo + (hi - lo) * ((float)((kk + 64) / 2 - clo) / (float)(chi - clo));
+        if (g > lo && g < hi) mid = g;
+      }
       if (it > 0 && !(mid > lo && mid < hi)) return false;
       const int c = wave_count_below(dv, mid);
       if (c >= kk && c <= 64) {
@@ -988,8 +1001,10 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
       if (c > 64) {
         if (it == 0) return false;
         hi = mid;
+        chi = c;
       } else {
         lo = mid;
+        clo = c;
       }
     }
     return false;
@@ -999,8 +1014,14 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
   bool wide = false;
   if (nA > 64) {
     const float hi = T;
-    if (!narrow(fmaxf(0.5f * T, __uint_as_float(0x40000001u)), hi)) {
-      if constexpr (WIDE) wide = narrow(0.f, hi);
+    if (!narrow(fmaxf(0.5f * T, __uint_as_float(0x40000001u)), hi, nA)) {
+      if constexpr (WIDE) {
+        // a wide support: the search starts just above the largest gap of a
+        // visible block, below which all nb visible blocks count
+        const float up = nextafterf(dlast, INFINITY);
+        const bool tight = up < hi;
+        wide = narrow(0.f, tight ? up : hi, tight ? nb : nA);
+      }
     }
   }
   if (nA <= 64) {
@@ -1034,10 +1055,16 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
     const double vi = ((double)si - dmax) * 0.5;
     const ulonglong2* key2 = reinterpret_cast<const ulonglong2*>(pb.key);
     int rank = 0;  // blocks of A ahead of this lane's in (score desc, index asc)
-#pragma unroll 2
-    for (int k4 = 0; k4 < nA4 / 4; ++k4) {
+    auto rank4 = [&](int k4) {
       const ulonglong2 a0 = key2[2 * k4], a1 = key2[2 * k4 + 1];
       rank += (a0.x > ki) + (a0.y > ki) + (a1.x > ki) + (a1.y > ki);
+    };
+    if constexpr (WIDE) {  // throughput use (prefill): fewer registers
+#pragma unroll 1
+      for (int k4 = 0; k4 < nA4 / 4; ++k4) rank4(k4);
+    } else {               // the decode step's latency path
+#pragma unroll 2
+      for (int k4 = 0; k4 < nA4 / 4; ++k4) rank4(k4);
     }
     double tau;
     if (!wide) {
