@@ -39,13 +39,13 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("c63d74cb602a3ad0", 45138123, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("c63d74cb602a3ad0", 18835928, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("c63d74cb602a3ad0", 892115157, 1024665),
-    ("uocr_rswa_step", "dense-1p-b512"): ("c63d74cb602a3ad0", 1092083624, 3940444),
-    ("uocr_rswa_step", "dense-40p-b32"): ("c63d74cb602a3ad0", 1699311165, 686684),
-    ("uocr_rswa_step", "dense-125p-b8"): ("c63d74cb602a3ad0", 1316296792, 302159),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("c63d74cb602a3ad0", 169109992, 167796425),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("930a9a5c20a5bf3e", 45167689, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("930a9a5c20a5bf3e", 18886072, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("930a9a5c20a5bf3e", 892115128, 1024662),
+    ("uocr_rswa_step", "dense-1p-b512"): ("930a9a5c20a5bf3e", 1092083450, 3940450),
+    ("uocr_rswa_step", "dense-40p-b32"): ("930a9a5c20a5bf3e", 1699311318, 686686),
+    ("uocr_rswa_step", "dense-125p-b8"): ("930a9a5c20a5bf3e", 1316296540, 302164),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("930a9a5c20a5bf3e", 169106821, 167786083),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
