@@ -941,9 +941,10 @@ __device__ __forceinline__ double wave_sum_d(double x) {
 // A then only has to hold the top kk, and the threshold comes from Newton's
 // method on h(tau) = || max(0, u - tau) ||_2 = 1 (a norm of convex functions
 // of tau, so convex, and decreasing: from tau = u_max - 1 the iterates rise
-// monotonically to the root; while the support holds still h is linear in
-// tau, where one step lands on the root), followed by
-// the closed form of the sorted algorithm on the support S = {u > tau} found,
+// monotonically to the root; for equal u on a fixed support h is linear in
+// tau and one step lands on the root, and near-flat supports take a few),
+// followed by the closed form of the sorted algorithm on the support
+// S = {u > tau} found,
 // accepted only if it satisfies the optimality conditions (u > tau_S on S,
 // u <= tau_S off S), which single out the exact support.
 template <int NS, bool WIDE = false>
@@ -1560,13 +1561,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
 // ---------------------------------------------------------------------------
 // uocr_prefill_route: the routing of a prefill chunk.  A workgroup takes qt
 // consecutive queries of one unit:
-//   1. q_idx = P^T q of each query (fp64, one thread per (query, index dim));
+//   1. q_idx = P^T q of each query on the fp64 matrix cores;
 //   2. the scores of every block visible to the tile's last query against the
-//      tile's queries (fp64, rounded once, into LDS); each thread holds one
-//      block key in registers and runs it against every query that may see it;
-//   3. each wave routes its queries (w, w + 8, ...) on the one-wave path.
-// A query that path cannot take (more than 1024 visible blocks, or more than
-// 64 candidates) is marked in sel_idx[0] and routed by k_prefill_fallback,
+//      tile's queries, as 16 x 16 fp64 matrix tiles (rounded once, into LDS);
+//   3. wave w routes query w on the one-wave path, then claims the next
+//      unrouted query of the tile.
+// A query that path cannot take (more than 1024 visible blocks, more than 64
+// blocks tied around the k-th score, or a wide support whose optimality check
+// fails) is marked in sel_idx[0] and routed by k_prefill_fallback,
 // which runs next in the same stream with the whole workgroup per query (its
 // register needs would halve this kernel's occupancy).  Query i of the chunk
 // sits at position q_pos[b] + i and sees the blocks all of whose prefix tokens
