@@ -665,9 +665,11 @@ __device__ __forceinline__ void reduce_scatter(double (&v)[N / 2], int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// uocr_block_index_build: each wave owns a contiguous run of (unit, block)
-// items and streams it, loading the next block's rows while it reduces the
-// current one; fp64 accumulation.  Per block: the row sums of every lane's
+// uocr_block_index_build / _range: each wave owns a contiguous run of
+// (unit, block in [first_block, first_block + n_blocks)) items and streams
+// it, loading the next block's rows while it reduces the current one; fp64
+// accumulation, in an order that does not depend on the range, so a rebuilt
+// block is bit-identical to its full-build value.  Per block: the row sums of every lane's
 // dimensions (exchanged between the row groups of the wave), then the
 // projection with P held transposed in LDS (Pt[i][d], rows padded by 4 floats
 // so the 16-byte reads and the transposing stores spread over the banks):
