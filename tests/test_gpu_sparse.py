@@ -38,7 +38,7 @@ def _check_selection(got_idx, got_prob, got_bias, s32, k, s64=None, eps=None, wh
     # itself they may differ from the oracle's by the certified bound eps;
     # p = (s/2 - tau)^2 moves by at most 2 * max|ds| (|s/2 - tau| <= 1 and tau
     # moves by at most max|ds|/2).
-    ptol = PROB_TOL if eps is None else PROB_TOL + 2.0 * float(np.max(eps))
+    ptol = PROB_TOL if eps is None else PROB_TOL + 2.0 * float(np.max(eps, initial=0.0))
     np.testing.assert_allclose(got_prob, prob, atol=ptol, err_msg=what)
     big = prob > 1e-3
     np.testing.assert_allclose(got_bias[big], bias[big], atol=BIAS_TOL + ptol / 1e-3, err_msg=what)
@@ -260,6 +260,19 @@ def test_srswa_wide_support_and_ragged(fused):
     _run_sparse(w, steps=4, fused=fused, t_gen=[0, 9, 500], flat=True)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_srswa_per_sequence_prefix_lengths(fused):
+    """One batch whose sequences have their own prefix lengths: none, one
+    token, one token into the second block, a prefix ending inside a block and
+    the full prefix.  Rows past each prefix hold NaN, so a read of one would
+    show in the output."""
+    need_gpu()
+    w = _small_sparse(batch=5, pages=4, prompt=9, planted=3, t0=0)
+    plens = [0, 1, 33, 500, w.prefix_len]
+    say("srswa per-sequence prefixes", plens, "fused" if fused else "")
+    _run_sparse(w, steps=3, fused=fused, t_gen=[0, 5, 127, 128, 400], plens=plens)
+
+
 # unusual shapes: head dims, dtypes, windows from 1 to 1024 slots, top-k from
 # 1 to 64, prefixes that end inside a block, counts before / across a wrap
 _SWEEP = [
@@ -283,14 +296,21 @@ def test_srswa_shape_sweep(cfg, fused):
     _run_sparse(w, steps=3, fused=fused, t_gen=t_gen)
 
 
-def _run_sparse(w, steps, units=None, num_splits=0, k=None, fused=False, t_gen=None, flat=False):
+def _run_sparse(w, steps, units=None, num_splits=0, k=None, fused=False, t_gen=None, flat=False, plens=None):
     kv = S.prefix_kv(w)
     if flat:   # shrink the keys so that block scores are close together (wide support)
         Kf = S.widen(kv[0], w.dtype) * 0.05
         kv = (S.store(Kf.astype(np.float32), w.dtype), kv[1])
+    if plens is not None:   # rows past each sequence's own prefix hold NaN: never read
+        for b, m in enumerate(plens):
+            kv[0][b, :, m:] = S.NAN_BITS[w.dtype]
+            kv[1][b, :, m:] = S.NAN_BITS[w.dtype]
     ring = S.initial_ring(w, t_gen)
     sess = DecodeSession(w, prefix_kv=kv, ring=ring, num_splits=num_splits, fused=fused)
     host = HostMirror(w, prefix_kv=kv, ring=ring)
+    if plens is not None:
+        sess.prefix_len.copy_(torch.tensor(plens, dtype=torch.int32))
+        host.prefix_len = np.asarray(plens)
     del kv
     sess.build_index()
     P = S.projection(w).astype(np.float64)
