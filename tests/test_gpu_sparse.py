@@ -273,6 +273,28 @@ def test_srswa_per_sequence_prefix_lengths(fused):
     _run_sparse(w, steps=3, fused=fused, t_gen=[0, 5, 127, 128, 400], plens=plens)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_srswa_over_1024_blocks(fused):
+    """130 pages (1040 blocks): past the one-wave routing, so the whole
+    workgroup routes before the live blocks are read."""
+    need_gpu()
+    w = _small_sparse(batch=2, heads=2, pages=130, planted=4, t0=0)
+    say("srswa 1040 blocks", "fused" if fused else "")
+    _run_sparse(w, steps=2, fused=fused, t_gen=[3, 300])
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_srswa_all_blocks_tied(fused):
+    """Every block scores the same, so more than 64 blocks tie at the k-th
+    score and the one-wave routing hands over to the workgroup path.  Entmax is
+    uniform (p = 1/nb on every block) and the first 16 blocks by index are
+    selected, all of them live."""
+    need_gpu()
+    w = _small_sparse(batch=2, heads=2, pages=13, planted=0, t0=0)
+    say("srswa tied blocks", "fused" if fused else "")
+    _run_sparse(w, steps=2, fused=fused, t_gen=[0, 200], tied=True)
+
+
 # unusual shapes: head dims, dtypes, windows from 1 to 1024 slots, top-k from
 # 1 to 64, prefixes that end inside a block, counts before / across a wrap
 _SWEEP = [
@@ -296,11 +318,15 @@ def test_srswa_shape_sweep(cfg, fused):
     _run_sparse(w, steps=3, fused=fused, t_gen=t_gen)
 
 
-def _run_sparse(w, steps, units=None, num_splits=0, k=None, fused=False, t_gen=None, flat=False, plens=None):
+def _run_sparse(w, steps, units=None, num_splits=0, k=None, fused=False, t_gen=None, flat=False, plens=None,
+                tied=False):
     kv = S.prefix_kv(w)
     if flat:   # shrink the keys so that block scores are close together (wide support)
         Kf = S.widen(kv[0], w.dtype) * 0.05
         kv = (S.store(Kf.astype(np.float32), w.dtype), kv[1])
+    if tied:   # every block's keys are block 0's: all block scores tie exactly
+        nbk = w.prefix_len // w.block
+        kv = (np.ascontiguousarray(np.tile(kv[0][:, :, :w.block], (1, 1, nbk, 1))), kv[1])
     if plens is not None:   # rows past each sequence's own prefix hold NaN: never read
         for b, m in enumerate(plens):
             kv[0][b, :, m:] = S.NAN_BITS[w.dtype]
