@@ -39,13 +39,13 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("3d4955111898fa83", 45167693, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("3d4955111898fa83", 18886111, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("3d4955111898fa83", 892115192, 1024643),
-    ("uocr_rswa_step", "dense-1p-b512"): ("3d4955111898fa83", 1092083418, 3940444),
-    ("uocr_rswa_step", "dense-40p-b32"): ("3d4955111898fa83", 1699311072, 686692),
-    ("uocr_rswa_step", "dense-125p-b8"): ("3d4955111898fa83", 1316296775, 302161),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("3d4955111898fa83", 169106933, 167788083),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("dd52353148606a1a", 45150538, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("dd52353148606a1a", 18888158, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("dd52353148606a1a", 892130898, 1024659),
+    ("uocr_rswa_step", "dense-1p-b512"): ("dd52353148606a1a", 1092091722, 3940456),
+    ("uocr_rswa_step", "dense-40p-b32"): ("dd52353148606a1a", 1699319553, 686726),
+    ("uocr_rswa_step", "dense-125p-b8"): ("dd52353148606a1a", 1316311949, 302161),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("dd52353148606a1a", 169110008, 167815994),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
