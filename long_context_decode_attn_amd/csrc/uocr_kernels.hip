@@ -2012,16 +2012,20 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   }
 
   // the first two batches of block keys (rows < nb_cap: no wait for
-  // prefix_len), in flight while q_idx is formed
+  // prefix_len), in flight while q_idx is formed.  The loads are
+  // unconditional, so that the compiler keeps them all in flight and waits
+  // for P and q alone before q_idx (with a branch around a load it waited
+  // for the load where the paths join): rows past nb_cap read the last row
+  // again, and without a prefix the first row of P stands in for the keys
+  // (no score is stored for any of these).
   const int kr = tid / 8, kc = tid % 8;
-  const float* K = a.kbar + (size_t)unit * a.nb_cap * kIdxDim + kc * 4;
+  const int last_row = max(a.nb_cap - 1, 0);
+  const float* K = (a.nb_cap > 0 ? a.kbar + (size_t)unit * a.nb_cap * kIdxDim : a.proj) + kc * 4;
   auto load_keys = [&](float4 (&dst)[KB], int jb) {
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
-      const int j = jb + u * RPP + kr;
-      dst[u] = j >= a.nb_cap ? make_float4(0.f, 0.f, 0.f, 0.f)
-               : STREAM ? ld16f_stream(K + (size_t)j * kIdxDim)
-                        : *reinterpret_cast<const float4*>(K + (size_t)j * kIdxDim);
+      const float* row = K + (size_t)min(jb + u * RPP + kr, last_row) * kIdxDim;
+      dst[u] = STREAM ? ld16f_stream(row) : *reinterpret_cast<const float4*>(row);
     }
   };
   float4 kvA[KB], kvB[KB];
