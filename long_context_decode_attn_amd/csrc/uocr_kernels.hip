@@ -1975,23 +1975,18 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   const DecodeArgs& d = a.d;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x, b = unit / d.heads, h = unit - b * d.heads;
-  const int m = min(max(d.prefix_len[b], 0), d.prefix_cap);
-  const int t = max(a.t_gen_in[b], 0);
-  const int n = d.window, slot = t % n, w = min(n, t + 1);
-  const int nb = (m + kBlock - 1) / kBlock;
   const int grp = lane / G::LPR, c = lane % G::LPR;
   const size_t cb = (size_t)c * 16;
 
-  // ring append of this unit's row
+  // The loads that depend on nothing but the unit go out first, in order:
+  // the new token's row (stored into its ring slot once the count is known),
+  // P and q for q_idx, the block keys.  Every lane issues each of them (the
+  // lanes past the new row re-read its last chunk), so that no per-lane
+  // branch makes the compiler wait for a load where the paths join.
   constexpr int CPR = G::ROWB / 16;
-  if (tid < 2 * CPR) {
-    const int which = tid / CPR, off = tid - which * CPR;
-    const char* src = static_cast<const char*>(which ? a.v_new : a.k_new) + (size_t)unit * G::ROWB + off * 16;
-    char* dst = static_cast<char*>(which ? a.v_ring : a.k_ring) + ((size_t)unit * n + slot) * G::ROWB + off * 16;
-    *reinterpret_cast<uint4*>(dst) = ld16(src);
-  }
-  if (h == 0 && tid == 0) a.t_gen_out[b] = t + 1;
-  if (tid == 0) tsm.flag = 0;  // zeroed before the first workgroup barrier
+  const int a_which = min(tid, 2 * CPR - 1) / CPR, a_off = min(tid, 2 * CPR - 1) - a_which * CPR;
+  const uint4 new_chunk =
+      ld16(static_cast<const char*>(a_which ? a.v_new : a.k_new) + (size_t)unit * G::ROWB + a_off * 16);
 
   // q_idx partial sums: the loads of P and q go out first, so that they are
   // not queued behind the block keys
@@ -2032,12 +2027,24 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   load_keys(kvA, 0);
   load_keys(kvB, RPP * KB);
 
+  const int m = min(max(d.prefix_len[b], 0), d.prefix_cap);
+  const int t = max(a.t_gen_in[b], 0);
+  const int n = d.window, slot = t % n, w = min(n, t + 1);
+  const int nb = (m + kBlock - 1) / kBlock;
+
   {
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < DPS; ++k) acc += (double)pv[k] * (double)qv_[k];
     s_red[sl_q][i_q] = acc;
   }
+
+  // ring append of this unit's row, and the new count
+  if (tid < 2 * CPR)
+    *reinterpret_cast<uint4*>(static_cast<char*>(a_which ? a.v_ring : a.k_ring) +
+                              ((size_t)unit * n + slot) * G::ROWB + a_off * 16) = new_chunk;
+  if (h == 0 && tid == 0) a.t_gen_out[b] = t + 1;
+  if (tid == 0) tsm.flag = 0;  // zeroed before the first workgroup barrier
 
   float q[G::E];
   load_q<DT, D>(d.q, unit, c, d.qscale, q);
