@@ -39,13 +39,13 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("dd52353148606a1a", 45150538, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("dd52353148606a1a", 18888158, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("dd52353148606a1a", 892130898, 1024659),
-    ("uocr_rswa_step", "dense-1p-b512"): ("dd52353148606a1a", 1092091722, 3940456),
-    ("uocr_rswa_step", "dense-40p-b32"): ("dd52353148606a1a", 1699319553, 686726),
-    ("uocr_rswa_step", "dense-125p-b8"): ("dd52353148606a1a", 1316311949, 302161),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("dd52353148606a1a", 169110008, 167815994),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("64fb36d3c9b6124e", 45145354, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("64fb36d3c9b6124e", 18882087, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("64fb36d3c9b6124e", 892130685, 1024661),
+    ("uocr_rswa_step", "dense-1p-b512"): ("64fb36d3c9b6124e", 1092091846, 3940455),
+    ("uocr_rswa_step", "dense-40p-b32"): ("64fb36d3c9b6124e", 1699319552, 686701),
+    ("uocr_rswa_step", "dense-125p-b8"): ("64fb36d3c9b6124e", 1316314341, 302168),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("64fb36d3c9b6124e", 169109970, 167825774),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
