@@ -253,7 +253,11 @@ struct State {
 // Row `srow` (if in range) is read from sK / sV instead of K / V.  Rows in
 // [nvalid, nrows) are read (they must be addressable) but carry no weight:
 // this lets a caller issue loads before it knows how many rows count.  U =
-// row loads of K and of V in flight per lane.
+// row loads of K and of V in flight per lane.  The K loads go out before the
+// V loads, and every lane issues all of them (a lane past the last row
+// re-reads row nrows - 1, with no weight): with no branch around a load the
+// compiler waits for each load only where its value is used, so the q.k
+// products start while the rest is in flight.
 template <int DT, int D, int U = Geo<DT, D>::U, bool STREAM = true>
 __device__ __forceinline__ void attend_range(const char* __restrict__ K, const char* __restrict__ V,
                                              int nrows, float bias2,
@@ -268,17 +272,15 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ K, const c
     uint4 kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = r0 + u * G::RPL + grp;
-      if (row < nrows) {
-        const bool sp = row == srow;
-        const char* kp = sp ? sK : K + (size_t)row * G::ROWB;
-        const char* vp = sp ? sV : V + (size_t)row * G::ROWB;
-        kr[u] = STREAM ? ld16_stream(kp) : ld16(kp);
-        vr[u] = STREAM ? ld16_stream(vp) : ld16(vp);
-      } else {
-        kr[u] = make_uint4(0u, 0u, 0u, 0u);
-        vr[u] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      const int row = min(r0 + u * G::RPL + grp, nrows - 1);
+      const char* kp = row == srow ? sK : K + (size_t)row * G::ROWB;
+      kr[u] = STREAM ? ld16_stream(kp) : ld16(kp);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = min(r0 + u * G::RPL + grp, nrows - 1);
+      const char* vp = row == srow ? sV : V + (size_t)row * G::ROWB;
+      vr[u] = STREAM ? ld16_stream(vp) : ld16(vp);
     }
     float s[U];
     float mt = kFloor;
