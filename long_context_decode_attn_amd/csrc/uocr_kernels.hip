@@ -315,6 +315,27 @@ __device__ __forceinline__ void attend_range(const char* __restrict__ K, const c
   }
 }
 
+// attend_range with no more loads in flight than the rows need (up to the
+// geometry's U): a short range (a live-block chunk, a window share) issues no
+// loads for rows past its end.
+template <int DT, int D, bool STREAM = true>
+__device__ __forceinline__ void attend_fit(const char* __restrict__ K, const char* __restrict__ V, int nrows,
+                                           float bias2, const float (&q)[Geo<DT, D>::E],
+                                           State<Geo<DT, D>::E>& st, int grp, int srow = -1,
+                                           const char* sK = nullptr, const char* sV = nullptr,
+                                           int nvalid = 1 << 30) {
+  using G = Geo<DT, D>;
+  const int need = (nrows + G::RPL - 1) / G::RPL;
+  if (G::U > 2 && need <= 2)
+    attend_range<DT, D, 2, STREAM>(K, V, nrows, bias2, q, st, grp, srow, sK, sV, nvalid);
+  else if (G::U > 4 && need <= 4)
+    attend_range<DT, D, 4, STREAM>(K, V, nrows, bias2, q, st, grp, srow, sK, sV, nvalid);
+  else if (G::U > 6 && need <= 6)
+    attend_range<DT, D, 6, STREAM>(K, V, nrows, bias2, q, st, grp, srow, sK, sV, nvalid);
+  else
+    attend_range<DT, D, G::U, STREAM>(K, V, nrows, bias2, q, st, grp, srow, sK, sV, nvalid);
+}
+
 // Merge the RPL row groups of a wave: afterwards every lane holds the wave's
 // state for its chunk.
 template <int OFF>
@@ -574,7 +595,7 @@ __global__ __launch_bounds__(256) void k_split_merge(DecodeArgs a) {
 // 32-row window chunks, dealt round-robin to the W waves.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
-__global__ __launch_bounds__(512) void k_srswa_decode(DecodeArgs a) {
+__global__ __launch_bounds__(512, 4) void k_srswa_decode(DecodeArgs a) {
   using G = Geo<DT, D>;
   __shared__ float lds_ml[kMaxWaves][2];
   __shared__ __attribute__((aligned(16))) float lds_o[kMaxWaves * D];
@@ -617,8 +638,8 @@ __global__ __launch_bounds__(512) void k_srswa_decode(DecodeArgs a) {
     const int r0 = wave * WR, nr = min(WR, w - r0);
     if (nr > 0) {
       const size_t base = ((size_t)unit * a.window + r0) * G::ROWB + cb;
-      attend_range<DT, D>(static_cast<const char*>(a.k_ring) + base,
-                          static_cast<const char*>(a.v_ring) + base, nr, 0.f, q, st, grp);
+      attend_fit<DT, D>(static_cast<const char*>(a.k_ring) + base, static_cast<const char*>(a.v_ring) + base,
+                        nr, 0.f, q, st, grp);
     }
   }
   if (wave >= l0 && n_live > 0) {
@@ -637,8 +658,8 @@ __global__ __launch_bounds__(512) void k_srswa_decode(DecodeArgs a) {
       const int nr = min(rpc, m - r0);
       if (nr <= 0) continue;
       const size_t base = ((size_t)unit * a.prefix_cap + r0) * G::ROWB + cb;
-      attend_range<DT, D>(static_cast<const char*>(a.k_prefix) + base,
-                          static_cast<const char*>(a.v_prefix) + base, nr, bj * kLog2e, q, st, grp);
+      attend_fit<DT, D>(static_cast<const char*>(a.k_prefix) + base, static_cast<const char*>(a.v_prefix) + base,
+                        nr, bj * kLog2e, q, st, grp);
     }
   }
   if (W == 8)
@@ -2144,8 +2165,8 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
     const int nr = min(rpc, m - r0);
     if (nr <= 0) continue;
     const size_t base = ((size_t)unit * d.prefix_cap + r0) * G::ROWB + cb;
-    attend_range<DT, D, G::U, STREAM>(static_cast<const char*>(d.k_prefix) + base,
-                                      static_cast<const char*>(d.v_prefix) + base, nr, bj * kLog2e, q, st, grp);
+    attend_fit<DT, D, STREAM>(static_cast<const char*>(d.k_prefix) + base,
+                              static_cast<const char*>(d.v_prefix) + base, nr, bj * kLog2e, q, st, grp);
   }
   wg_finish<DT, D, W>(st, lds_ml, lds_o, d, unit, 0);
 }
