@@ -39,13 +39,13 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("d739e8975a8c3401", 45120859, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("d739e8975a8c3401", 18879987, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("d739e8975a8c3401", 892194352, 1024672),
-    ("uocr_rswa_step", "dense-1p-b512"): ("d739e8975a8c3401", 1092830440, 3940462),
-    ("uocr_rswa_step", "dense-40p-b32"): ("d739e8975a8c3401", 1699302019, 686888),
-    ("uocr_rswa_step", "dense-125p-b8"): ("d739e8975a8c3401", 1316298696, 302167),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("d739e8975a8c3401", 169102789, 167787738),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("5222f959ef9337d1", 45184292, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("5222f959ef9337d1", 18925092, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("5222f959ef9337d1", 892196484, 1024679),
+    ("uocr_rswa_step", "dense-1p-b512"): ("5222f959ef9337d1", 1092833039, 3940461),
+    ("uocr_rswa_step", "dense-40p-b32"): ("5222f959ef9337d1", 1699310239, 686913),
+    ("uocr_rswa_step", "dense-125p-b8"): ("5222f959ef9337d1", 1316300224, 302178),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("5222f959ef9337d1", 169102797, 167847078),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
