@@ -1664,7 +1664,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kPrefillThreads = 512;
 constexpr int kPrefillScores = 12288;  // LDS score slots: qt x nb_cap
-constexpr int kPrefillTilesInFlight = 1;  // key tiles per wave with loads in flight (4 measured slower)
+constexpr int kPrefillTilesInFlight = 1;  // key tiles per wave with loads in flight (2 or 4 measured slower)
 constexpr int kPrefillMaxQ = 16;
 constexpr int32_t kDeferred = INT32_MIN;
 
@@ -1744,20 +1744,23 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
   const int lr = lane % 16, lk = lane / 16;
   const float* K = a.kbar + (size_t)t.unit * a.nb_cap * kIdxDim;
   const int ntiles = (nbmax + 15) / 16;
+  // The key tiles do not depend on q_idx: this wave's first tiles are loaded
+  // before it, and each tile consumed below puts the loads of the tile
+  // kPrefillTilesInFlight * W later in flight.  Every lane loads (blocks past
+  // the visible ones re-read the last visible one: their columns of the
+  // product are never stored), with no branch around a load, so the compiler
+  // waits for a tile only where it is used.
   auto load_b = [&](float4 (&bf)[2], int tile) {  // this lane's dims of one key of a tile
-    const int j = tile * 16 + lr;
-    const bool jok = j < nbmax;
-    const float4* kr = reinterpret_cast<const float4*>(K + (size_t)(jok ? j : 0) * kIdxDim) + lk;
-    bf[0] = jok ? kr[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-    bf[1] = jok ? kr[4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int j = min(tile * 16 + lr, max(nbmax - 1, 0));
+    const float4* kr = reinterpret_cast<const float4*>(K + (size_t)j * kIdxDim) + lk;
+    bf[0] = kr[0];
+    bf[1] = kr[4];
   };
-  // this wave's first kPrefillTilesInFlight key tiles do not depend on q_idx:
-  // their loads go first, and each tile consumed below puts the loads of the
-  // tile that many steps later in flight
   float4 bq[kPrefillTilesInFlight][2];
+  if (nbmax > 0) {
 #pragma unroll
-  for (int u = 0; u < kPrefillTilesInFlight; ++u)
-    if (wave + u * W < ntiles) load_b(bq[u], wave + u * W);
+    for (int u = 0; u < kPrefillTilesInFlight; ++u) load_b(bq[u], wave + u * W);
+  }
 
   // 1. q_idx on the matrix cores, fp64, with the operands read straight from
   //    global memory (P [D][32] is shared by every workgroup and stays in L2):
@@ -1816,7 +1819,7 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
         if (tile >= ntiles) break;
         const int j = tile * 16 + lr;
         const float4 b0 = bq[u][0], b1 = bq[u][1];
-        if (tile + NF * W < ntiles) load_b(bq[u], tile + NF * W);
+        load_b(bq[u], tile + NF * W);
         const float bf[kIdxDim / 4] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
         v4d acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
