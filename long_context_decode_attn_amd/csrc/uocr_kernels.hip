@@ -1976,13 +1976,16 @@ __global__ __launch_bounds__(kNgramThreads) void k_ngram_ban(NgramArgs a) {
 // STREAM selects nontemporal loads (better when the grid fills the chip and
 // the step is bandwidth-bound) or plain loads (lower latency, better for a
 // few units per CU).
-//   1. write the new token into its ring slot; issue the loads of the block
-//      keys; q_idx = P^T q (fp64);
+//   1. issue the loads of the new token's row, P, q and the block keys;
+//      q_idx = P^T q (fp64); write the new row into its ring slot;
 //   2. block scores into LDS;
 //   3. entmax + top-k on wave 0 while waves 1 .. W-1 attend over the window,
 //      which does not depend on the routing (the new token's row is taken
-//      from k_new / v_new, so no wave waits for the ring write);
-//   4. attend over the live selected blocks; merge the waves through LDS.
+//      from k_new / v_new, so no wave waits for the ring write); wave 0
+//      hands the selection over through an LDS flag, not a barrier;
+//   4. each wave attends over its share of the live selected blocks as soon
+//      as it has the selection and its window share is done; the waves merge
+//      through LDS.
 template <int DT, int D, int NT, bool STREAM>
 __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a) {
   using G = Geo<DT, D>;
