@@ -39,13 +39,13 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("398c7ece05980466", 45166893, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("398c7ece05980466", 18900322, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("398c7ece05980466", 892188527, 1024674),
-    ("uocr_rswa_step", "dense-1p-b512"): ("398c7ece05980466", 1092821502, 3940453),
-    ("uocr_rswa_step", "dense-40p-b32"): ("398c7ece05980466", 1699294859, 686880),
-    ("uocr_rswa_step", "dense-125p-b8"): ("398c7ece05980466", 1316291587, 302166),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("398c7ece05980466", 169078306, 167787187),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("5bfe89ffc2decf68", 45166878, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("5bfe89ffc2decf68", 18900476, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("5bfe89ffc2decf68", 892188055, 1024675),
+    ("uocr_rswa_step", "dense-1p-b512"): ("5bfe89ffc2decf68", 1092835108, 3940452),
+    ("uocr_rswa_step", "dense-40p-b32"): ("5bfe89ffc2decf68", 1699294832, 686865),
+    ("uocr_rswa_step", "dense-125p-b8"): ("5bfe89ffc2decf68", 1316291734, 302168),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("5bfe89ffc2decf68", 169078300, 167787446),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
