@@ -297,7 +297,8 @@ int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route,
  *   uocr_rswa_step  == uocr_ring_append then uocr_rswa_decode;
  *   uocr_srswa_step == uocr_ring_append then uocr_block_score,
  *                      uocr_entmax15_topk and uocr_srswa_decode,
- * with the same results (sel_idx / sel_prob / sel_bias / out), except that
+ * with the same results (sel_idx / sel_prob / sel_bias; out up to the order
+ * of its floating-point sums, which the waves split differently), except that
  * the generated-token counts are double-buffered: t_gen_in[b] is read,
  * t_gen_out[b] = t_gen_in[b] + 1 is written and t_gen_in is left unchanged,
  * so that no workgroup can see a count another one already advanced.  The
