@@ -46,3 +46,18 @@ def test_sparse_full_step_bytes():
     step = sum(b.values())
     assert abs(step / w.units - 372_992) / 372_992 < 2e-3
     assert abs(step / 1e6 - 119.4) < 0.3
+
+
+def test_counters_and_profiles_belong_to_this_kernel_source():
+    """The HBM traffic bench.py reports and the rocprofv3 summaries under
+    profiles/ name the kernel source they were taken on (a sha256 prefix of
+    uocr_kernels.hip); they must name the one in the tree, so that an edit of
+    the kernels is followed by new measurements."""
+    h = bench.kernel_source_hash()
+    assert bench.COUNTER_TRAFFIC and all(rec[0] == h for rec in bench.COUNTER_TRAFFIC.values())
+    prof = os.path.join(ROOT, "profiles")
+    names = sorted(f for f in os.listdir(prof) if f.endswith(".txt"))
+    assert names
+    for f in names:
+        with open(os.path.join(prof, f)) as fh:
+            assert f"kernel source sha256[:16]: {h}" in fh.read(), f
