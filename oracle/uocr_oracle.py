@@ -326,21 +326,6 @@ def srswa_unit(q, k_prefix, v_prefix, m, sel_idx, sel_bias, k_window, v_window,
     return attention(q, np.concatenate(Ks), np.concatenate(Vs), scale, np.concatenate(bs))
 
 
-def srswa_decode(q, k_prefix, v_prefix, prefix_len, sel_idx, sel_bias,
-                 ring_k, ring_v, t_gen, scale, block: int = 32) -> np.ndarray:
-    """Batched sparse decode: sel_idx / sel_bias [B][H][k]."""
-    B, H = q.shape[0], q.shape[1]
-    out = np.zeros(q.shape, dtype=F64)
-    for b in range(B):
-        m, t = int(prefix_len[b]), int(t_gen[b])
-        for h in range(H):
-            out[b, h] = srswa_unit(q[b, h], k_prefix[b, h], v_prefix[b, h], m, sel_idx[b, h],
-                                   None if sel_bias is None else sel_bias[b, h],
-                                   ring_window(ring_k[b, h], t), ring_window(ring_v[b, h], t),
-                                   scale, block)
-    return out
-
-
 # ============================================================================
 # Prefill-side routing   ([Unlimited OCR Works README mirror] SGLang server
 # section, notes on the memory knobs: the prefill holds a temporary score
@@ -488,9 +473,21 @@ def route(q, k_prefix, prefix_len, proj, k: int, block: int = 32):
 
 
 def score_error_bound(q: np.ndarray, proj: np.ndarray, kbar: np.ndarray) -> np.ndarray:
-    """Per-block bound on how far a float32-stored computation of s_j can be
-    from the exact value: 2^-22 * sum_i |(P^T q)_i| |kbar_ji| (four float32
-    roundings of every term) plus one float32 unit in the last place of s_j."""
+    """Per-block bound on how far a stored score s_j may lie from the exact
+    value (P^T q) . kbar_j when it is evaluated the way the routing's stored
+    scores are: the block key kbar_j is held in float32 (rounded once from a
+    float64 or exact value), q_idx = P^T q and the dot product are
+    accumulated in float64, and the result is rounded once to float32.
+
+        eps_j = 2^-22 * sum_i |q_idx_i| |kbar_ji|  +  ulp32(s_j)
+
+    Rounding kbar_ji to float32 moves the term q_idx_i kbar_ji by at most
+    2^-24 |q_idx_i| |kbar_ji|; the float64 sums add errors some 2^29 times
+    smaller for these magnitudes, which the factor 4 margin (2^-22) absorbs;
+    the final rounding moves the value by half a float32 ulp of the
+    pre-rounded value, at most one ulp of the exact one.  The bound is
+    within a factor 8 of the largest error such an evaluation can make on
+    the given values (tests/test_oracle_score_bound.py pins both sides)."""
     q_idx = np.asarray(proj, dtype=F64).T @ np.asarray(q, dtype=F64)
     s = np.asarray(kbar, dtype=F64) @ q_idx
     mag = np.abs(np.asarray(kbar, dtype=F64)) @ np.abs(q_idx)
@@ -498,11 +495,46 @@ def score_error_bound(q: np.ndarray, proj: np.ndarray, kbar: np.ndarray) -> np.n
     return 2.0 ** -22 * mag + ulp
 
 
+def certified_selection(s: np.ndarray, eps: np.ndarray, k: int):
+    """Which blocks every evaluation of the scores within the bounds selects,
+    and which none does (the certified-gap reading of the selection where
+    floating point decides it).  s = exact scores, eps = per-block bounds,
+    selection = the first min(k, nb) blocks by (score desc, index asc).
+
+    Block x is surely selected when fewer than k other blocks can reach its
+    lowest value s_x - eps_x (a block that reaches it exactly may win the tie
+    by index, so it counts); surely dropped when at least k blocks have a
+    lowest value above its highest value s_x + eps_x.
+    Returns (sure_in, sure_out) as boolean arrays [nb]."""
+    s = np.asarray(s, dtype=F64)
+    eps = np.asarray(eps, dtype=F64)
+    lo, hi = s - eps, s + eps
+    others = ~np.eye(len(s), dtype=bool)                      # pairs (x, y) with y != x
+    rivals = ((hi[None, :] >= lo[:, None]) & others).sum(axis=1)
+    above = ((lo[None, :] > hi[:, None]) & others).sum(axis=1)
+    return rivals < k, above >= k
+
+
 def ambiguous_boundary(s64: np.ndarray, eps: np.ndarray, k: int) -> bool:
-    """True when the block ranked k and the block ranked k+1 (by exact score)
-    are closer than their error bounds, so that either may be chosen."""
-    if len(s64) <= k:
+    """True when the bounds leave the selected set open: fewer than
+    min(k, nb) blocks are surely selected, so evaluations within the bounds
+    may select different sets (certified_selection says which)."""
+    sure_in, _ = certified_selection(s64, eps, k)
+    return int(sure_in.sum()) < min(k, len(s64))
+
+
+def selection_within_bounds(sel: np.ndarray, s64: np.ndarray, eps: np.ndarray, k: int) -> bool:
+    """Whether a selected index list (ascending, -1 padding) is one that an
+    evaluation within the bounds can give: min(k, nb) distinct blocks in
+    ascending order, every surely selected block in it, no surely dropped
+    one."""
+    sure_in, sure_out = certified_selection(s64, eps, k)
+    nb = len(s64)
+    want = min(k, nb)
+    sel = [int(j) for j in sel]
+    picked = sel[:want]
+    if any(j != -1 for j in sel[want:]):
         return False
-    order = sorted(range(len(s64)), key=lambda j: (-float(s64[j]), j))
-    a, b = order[k - 1], order[k]
-    return abs(s64[a] - s64[b]) <= eps[a] + eps[b]
+    if any(j < 0 or j >= nb for j in picked) or picked != sorted(set(picked)) or len(picked) != want:
+        return False
+    return all(j in picked for j in np.nonzero(sure_in)[0]) and not any(sure_out[j] for j in picked)

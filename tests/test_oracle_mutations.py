@@ -184,3 +184,55 @@ def test_rope_variant_without_mistake_passes():
 @pytest.mark.parametrize("mistake", ["swap_axes", "freq_over_d", "flip_sin", "no_mod", "interleaved"])
 def test_rope_mistakes_are_caught(mistake):
     _fails(T.check_rope, rope_page2d=_rope_variant(**{mistake: True}))
+
+
+# ----------------------------------------------------------------------------
+# the certified score bound and the selection rule built on it
+# ----------------------------------------------------------------------------
+from tests import test_oracle_score_bound as B   # noqa: E402
+
+
+def test_score_bound_too_loose_is_caught():
+    _fails(B.check_bound_tight, score_error_bound=lambda q, P, kb: O.score_error_bound(q, P, kb) * 2.0 ** 8)
+
+
+def test_score_bound_too_tight_is_caught():
+    def too_tight(q, P, kb):
+        qi = np.asarray(P, float).T @ np.asarray(q, float)
+        s = np.asarray(kb, float) @ qi
+        return 2.0 ** -26 * (np.abs(kb) @ np.abs(qi)) + np.spacing(np.abs(s).astype(np.float32)).astype(float) / 4
+    _fails(B.check_bound_sound, score_error_bound=too_tight)
+
+
+def test_score_bound_relative_to_the_score_is_caught():
+    """A bound proportional to |s| instead of the sum of |terms| fails where
+    the score cancels to near 0."""
+    def relative(q, P, kb):
+        qi = np.asarray(P, float).T @ np.asarray(q, float)
+        s = np.asarray(kb, float) @ qi
+        return 2.0 ** -22 * np.abs(s) + np.spacing(np.abs(s).astype(np.float32)).astype(float)
+    _fails(B.check_bound_sound, score_error_bound=relative)
+
+
+def test_selection_rule_comparing_only_ranks_k_and_k_plus_1_is_caught():
+    """The pairwise reading (flag only when the blocks ranked k and k + 1 are
+    within their bounds) misses swaps deeper in the ranking when the bounds
+    differ between blocks."""
+    def pairwise(s, eps, k):
+        if len(s) <= k:
+            return False
+        order = sorted(range(len(s)), key=lambda j: (-float(s[j]), j))
+        a, b = order[k - 1], order[k]
+        return abs(s[a] - s[b]) <= eps[a] + eps[b]
+    _fails(B.check_selection_rule, ambiguous=pairwise)
+
+
+def test_selection_rule_ignoring_index_ties_is_caught():
+    """Counting only rivals strictly above a block's lowest value forgets that
+    an exact tie goes to the lower index."""
+    def strict(s, eps, k):
+        lo, hi = np.asarray(s) - eps, np.asarray(s) + eps
+        others = ~np.eye(len(s), dtype=bool)
+        return (((hi[None, :] > lo[:, None]) & others).sum(1) < k,
+                ((lo[None, :] > hi[:, None]) & others).sum(1) >= k)
+    _fails(B.check_selection_rule, certified_selection=strict)

@@ -398,6 +398,47 @@ def test_route_end_to_end_planted_support():
             assert abs(p.sum() - 1) < 1e-12
 
 
+def check_route(route=O.route):
+    """The batched routing against explicit loops and enumeration, on
+    small-integer inputs where every block key and score is exact: block
+    keys as per-token sums of P^T k averaged over the block (partial last
+    blocks included), scores as plain sums, the top-k by a full sort of
+    (-score, index) and 1.5-entmax by enumerating support sets."""
+    rng = np.random.default_rng(41)
+    B, H, D, d, k = 2, 2, 6, 4, 3
+    P = rng.integers(-2, 3, size=(D, d)).astype(float)
+    m_cap = 7 * 32
+    K = rng.integers(-3, 4, size=(B, H, m_cap, D)).astype(float)
+    q = rng.integers(-2, 3, size=(B, H, D)).astype(float) / 8.0
+    for plens in ([m_cap, 40], [0, 97]):
+        res = route(q, K, np.array(plens), P, k)
+        for b in range(B):
+            m = plens[b]
+            nb = -(-m // 32)
+            for h in range(H):
+                kbar = []
+                for j in range(nb):
+                    toks = range(32 * j, min(32 * j + 32, m))
+                    kbar.append([sum(sum(P[t, i] * K[b, h, r, t] for t in range(D)) for r in toks) / len(toks)
+                                 for i in range(d)])
+                qi = [sum(P[t, i] * q[b, h, t] for t in range(D)) for i in range(d)]
+                sc = np.array([sum(qi[i] * kbar[j][i] for i in range(d)) for j in range(nb)])
+                assert np.array_equal(res["s32"][b, h], sc), (b, h)
+                sel, p = _route_by_enumeration(sc, k)
+                want = np.full(k, -1)
+                want[:len(sel)] = sel
+                assert np.array_equal(res["idx"][b, h], want), (b, h, res["idx"][b, h], want)
+                for a, j in enumerate(sel):
+                    assert abs(res["prob"][b, h, a] - p[j]) < 1e-12
+                    lp = res["bias"][b, h, a]
+                    assert (lp == -math.inf) if p[j] == 0 else abs(lp - math.log(p[j])) < 1e-12
+                assert (res["prob"][b, h, len(sel):] == 0).all() and np.isneginf(res["bias"][b, h, len(sel):]).all()
+
+
+def test_route_against_enumeration():
+    check_route()
+
+
 def test_ambiguity_rule_flags_only_near_ties():
     s = np.array([5.0, 3.0, 3.0 + 1e-9, 1.0])
     eps = np.full(4, 1e-7)
