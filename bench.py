@@ -57,7 +57,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=2400)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="srswa-40p-b32")
-    ap.add_argument("--layers", type=int, default=12, help="independent per-layer states cycled by the steps")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="independent per-layer states cycled by the steps (0: enough that their working set is "
+                         "twice the 256 MB Infinity Cache, at least 12)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--t0", type=int, default=None,
                     help="generated tokens before the first step (default: the workload's; for flatness runs)")
@@ -74,6 +76,9 @@ def parse():
     ap.add_argument("--rope-page2d", type=int, default=0, metavar="TQ",
                     help="instead of the decode step, time uocr_rope_page2d over the keys of a prefill chunk of TQ "
                          "tokens per (sequence, head) of the workload (page_mod 2, base 10000)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="instead of the decode step, measure the denominators: plain and nontemporal read "
+                         "streams over 2 GiB, empty launches and per-workgroup pulls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (known bytes) so that a "
                          "counter profile of this run can scale FETCH_SIZE / WRITE_SIZE")
@@ -121,56 +126,90 @@ def index_bytes(w):
 # ----------------------------------------------------------------------------
 # CPU oracle baseline on a bounded sample
 # ----------------------------------------------------------------------------
-def cpu_baseline(w, budget_s: float):
-    """Time the oracle's decode step (append, score from the prebuilt block
-    index, entmax top-k, sparse or dense attention) on a sample of units, one
-    unit-step at a time, until the time budget is spent."""
+def host_cores() -> int:
+    """Host threads this process may use (its CPU affinity), at most 16: the
+    host share of one GPU on the boxes this runs on."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_unit_steps(w, b, h, budget_s):
+    """One (sequence, head) unit's decode steps with the oracle (append,
+    scores from the prebuilt block index, entmax top-k, sparse or dense
+    attention), one thread, until the budget is spent; returns (steps, s)."""
     from threadpoolctl import threadpool_limits
 
     from long_context_decode_attn_amd import synth as S
     from oracle import uocr_oracle as O
 
-    rng = np.random.default_rng(0)
-    n_sample = 4
-    seqs = sorted(set(int(x) for x in rng.choice(w.batch, size=min(n_sample, w.batch), replace=False)))
     P = S.projection(w).astype(np.float64) if w.sparse else None
-    units = []
-    for b in seqs:
-        Kp, Vp = S.prefix_kv_seq(w, b)
-        Kp, Vp = S.widen(Kp, w.dtype), S.widen(Vp, w.dtype)
-        h = int(rng.integers(w.heads))
-        Kr, Vr, t_gen = S.initial_ring(w)
-        u = {"b": b, "h": h, "Kp": Kp[h], "Vp": Vp[h],
-             "Kr": S.widen(Kr[b:b + 1, h:h + 1], w.dtype), "Vr": S.widen(Vr[b:b + 1, h:h + 1], w.dtype),
-             "t": t_gen[b:b + 1].astype(np.int64).copy()}
-        if w.sparse:
-            u["kbar"] = O.block_index(u["Kp"], w.prefix_len, P)   # one-time, not timed
-        units.append(u)
+    Kp, Vp = S.prefix_kv_seq(w, b)
+    Kp, Vp = S.widen(Kp[h], w.dtype), S.widen(Vp[h], w.dtype)
+    Kr, Vr, t_gen = S.initial_ring(w)
+    Kr, Vr = S.widen(Kr[b:b + 1, h:h + 1], w.dtype), S.widen(Vr[b:b + 1, h:h + 1], w.dtype)
+    t = t_gen[b:b + 1].astype(np.int64).copy()
+    kbar = O.block_index(Kp, w.prefix_len, P) if w.sparse else None   # one-time, not timed
+    pool = []   # this unit's inputs of 16 steps, cycled (drawn before timing)
+    for i in range(16):
+        q, k, v = S.step_inputs(w, i)
+        pool.append((S.widen(q[b, h], w.dtype), S.widen(k[b:b + 1, h:h + 1], w.dtype),
+                     S.widen(v[b:b + 1, h:h + 1], w.dtype)))
     done = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        step = 0
         while time.perf_counter() - t0 < budget_s:
-            q, k, v = S.step_inputs(w, step)
-            for u in units:
-                b, h = u["b"], u["h"]
-                O.ring_append(u["Kr"], u["Vr"], u["t"], S.widen(k[b:b + 1, h:h + 1], w.dtype),
-                              S.widen(v[b:b + 1, h:h + 1], w.dtype))
-                qd = S.widen(q[b, h], w.dtype)
-                t = int(u["t"][0])
-                wk, wv = O.ring_window(u["Kr"][0, 0], t), O.ring_window(u["Vr"][0, 0], t)
-                if w.sparse:
-                    s32 = O.as_f32(O.block_scores(qd, P, u["kbar"]))
-                    idx, _, bias = O.route_unit(s32, w.topk)
-                    O.srswa_unit(qd, u["Kp"], u["Vp"], w.prefix_len, idx, bias, wk, wv, w.scale)
-                else:
-                    O.rswa_unit(qd, u["Kp"], u["Vp"], w.prefix_len, wk, wv, w.scale)
-                done += 1
-            step += 1
-        dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": UNIT, "cores": 1, "kind": "oracle",
-            "sample": f"{done} unit-steps ({len(units)} (sequence, head) units x {step} steps) of {w.name} "
-                      f"in {dt:.1f} s, float64 numpy, 1 thread; block index built before timing"}
+            qd, k, v = pool[done % len(pool)]
+            O.ring_append(Kr, Vr, t, k, v)
+            wk, wv = O.ring_window(Kr[0, 0], int(t[0])), O.ring_window(Vr[0, 0], int(t[0]))
+            if w.sparse:
+                s32 = O.as_f32(O.block_scores(qd, P, kbar))
+                idx, _, bias = O.route_unit(s32, w.topk)
+                O.srswa_unit(qd, Kp, Vp, w.prefix_len, idx, bias, wk, wv, w.scale)
+            else:
+                O.rswa_unit(qd, Kp, Vp, w.prefix_len, wk, wv, w.scale)
+            done += 1
+        return done, time.perf_counter() - t0
+
+
+def _oracle_worker(arg):
+    w, b, h, budget_s = arg
+    return _oracle_unit_steps(w, b, h, budget_s)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle timed on the host: one thread on one unit, then every
+    usable host core at once, one unit per core (processes forked before the
+    GPU is touched).  value = the all-cores rate in unit-steps per second."""
+    import multiprocessing as mp
+
+    rng = np.random.default_rng(0)
+    cores = host_cores()
+    units = [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(cores)]
+    n1, dt1 = _oracle_unit_steps(w, units[0][0], units[0][1], budget_s / 3)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_oracle_worker, [(w, b, h, 2 * budget_s / 3) for b, h in units])
+    wall = time.perf_counter() - t0
+    done = sum(r[0] for r in res)
+    rate = done / max(r[1] for r in res)
+    return {"value": rate, "unit": UNIT, "cores": cores, "kind": "oracle",
+            "single_thread_value": n1 / dt1, "cpu_model": cpu_model(),
+            "sample": f"{w.name}: {done} unit-steps on {cores} processes of one thread each, one (sequence, head) "
+                      f"unit per process ({wall:.1f} s wall, {2 * budget_s / 3:.1f} s of steps each); one thread "
+                      f"alone: {n1} unit-steps in {dt1:.1f} s; float64 numpy; block index built before timing"}
 
 
 # ----------------------------------------------------------------------------
@@ -476,6 +515,77 @@ def rope_cpu_baseline(w, page, offset, budget_s):
 
 
 # ----------------------------------------------------------------------------
+# calibration: attainable read bandwidth, launch floor, per-workgroup pull
+# ----------------------------------------------------------------------------
+def _graph_time_us(fn, per_graph=32, reps=20):
+    """Average time of fn() replayed from a HIP graph of per_graph calls."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (per_graph * reps)
+
+
+def calibrate_main(args):
+    """Denominators measured on this machine: a plain and a nontemporal read
+    stream over 2 GiB, an empty launch at the decode steps' grids, and the
+    time workgroups take to pull their own bytes when only some compute
+    units are busy (uocr_calib_* in include/uocr_calib.h)."""
+    import torch
+
+    from long_context_decode_attn_amd import uocr as U
+    U.load_library()
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    out = {"metric": "calibration", "peak_gbs": HBM_PEAK_GBS, "stream_bytes": nbytes}
+    for nt in (False, True):
+        us = _graph_time_us(lambda: U.uocr_calib_read(src, nt, sink), per_graph=4, reps=10)
+        out[f"read_{'nontemporal' if nt else 'plain'}_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        print(json.dumps({"step": "read", "nontemporal": nt, "us": round(us, 2)}), flush=True)
+    out["empty_launch_us"] = {}
+    for groups, threads in [(1, 64), (80, 512), (320, 512), (2560, 256), (10240, 256)]:
+        out["empty_launch_us"][f"{groups}x{threads}"] = round(
+            _graph_time_us(lambda: U.uocr_calib_empty(groups, threads)), 3)
+    print(json.dumps({"step": "empty", **out["empty_launch_us"]}), flush=True)
+    pull = {}
+    for groups in (80, 256, 320, 640):
+        sk = torch.zeros(groups, dtype=torch.int32, device="cuda")
+        for kb in (16, 64, 128, 256):
+            per = kb * 1024
+            # rotate over disjoint regions of the 2 GiB buffer, at least twice the
+            # 256 MB Infinity Cache in all, so that the reads come from HBM
+            regions = max(1, nbytes // (groups * per))
+            want = max(8, -(-(512 << 20) // (groups * per)))
+            views = [src[r * groups * per:(r + 1) * groups * per] for r in range(min(regions, want))]
+            state = {"i": 0}
+
+            def call():
+                v = views[state["i"] % len(views)]
+                state["i"] += 1
+                U.uocr_calib_pull(v, per, groups, 512, True, sk)
+            us = _graph_time_us(call, per_graph=len(views), reps=10)
+            pull[f"{groups}x{kb}KiB"] = {"us": round(us, 3), "gbs": round(groups * per / (us * 1e-6) / 1e9, 1),
+                                         "per_group_gbs": round(per / (us * 1e-6) / 1e9, 2)}
+        print(json.dumps({"step": "pull", "groups": groups}), flush=True)
+    out["pull_512_threads_nontemporal"] = pull
+    print(json.dumps(out), flush=True)
+
+
+# ----------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1:
@@ -483,6 +593,8 @@ def main():
               f"cross-GPU step; see DESIGN.md for how it would shard.", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate:
+        return calibrate_main(args)
     if args.prefill_route:
         return prefill_main(args)
     if args.rope_page2d:
@@ -490,82 +602,83 @@ def main():
     if args.ngram_ban:
         return ngram_main(args)
 
+    from long_context_decode_attn_amd import synth as S
+    w = S.WORKLOADS[args.workload]
+    if args.t0 is not None:
+        w = w.replace(t0=args.t0)
+    # the CPU baseline forks its worker processes before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+
     import torch
 
-    from long_context_decode_attn_amd import synth as S
     from long_context_decode_attn_amd import uocr as U
-    from long_context_decode_attn_amd.session import DecodeSession, to_device
+    from long_context_decode_attn_amd.runner import LayeredDecoder, layers_for
+    from long_context_decode_attn_amd.session import DecodeSession
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     U.load_library()
     torch.cuda.set_device(0)
-    w = S.WORKLOADS[args.workload]
-    if args.t0 is not None:
-        w = w.replace(t0=args.t0)
     t_setup = time.perf_counter()
     fused = args.mode == "fused"
     base = DecodeSession(w, num_splits=args.num_splits, fused=fused)
-    layers = [base] + [base.clone() for _ in range(args.layers - 1)]
+    if w.sparse:
+        base.build_index()   # the first launch also loads the kernel; the build is timed below
+
+    # layers: enough that the steps' working set is twice the Infinity Cache;
+    # the sparse step's bytes depend on the live blocks, measured on one step
+    # of a scratch copy
+    live_est = None
+    if w.sparse:
+        probe = base.clone()
+        from long_context_decode_attn_amd.session import to_device
+        q, k, v = S.step_inputs(w, 0)
+        probe.step(to_device(q, w.dtype), to_device(k, w.dtype), to_device(v, w.dtype))
+        live_est = int(np.sum((probe.sel_idx.cpu().numpy() >= 0) & np.isfinite(probe.sel_bias.cpu().numpy())))
+        del probe
+    est_bytes = sum(algorithmic_bytes(w, live_est).values())
+    n_layers = args.layers if args.layers > 0 else layers_for(est_bytes)
+    dec = LayeredDecoder(w, n_layers, num_splits=args.num_splits, fused=fused, base=base)
     torch.cuda.synchronize()
 
     # one-time block index per layer (timed on its own, reported separately)
     idx_ms = None
     if w.sparse:
-        layers[0].build_index()  # first launch loads the kernel; not part of the build's cost
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for s in layers:
-            s.build_index()
+        dec.build_index()
         e1.record()
         torch.cuda.synchronize()
-        idx_ms = e0.elapsed_time(e1) / len(layers)
+        idx_ms = e0.elapsed_time(e1) / dec.L
 
     if args.copy_calibration:
         calibration_copy()
-
-    pool_n = 64
-    qp, kp, vp = S.step_pool(w, pool_n)
-    pool = [(to_device(qp[i], w.dtype), to_device(kp[i], w.dtype), to_device(vp[i], w.dtype)) for i in range(pool_n)]
+    dec.fill_pool(64)
     setup_s = time.perf_counter() - t_setup
 
-    def run_step(i):
-        s = layers[i % len(layers)]
-        q, k, v = pool[i % pool_n]
-        s.step(q, k, v)
-
-    for i in range(args.warmup):
-        run_step(i)
+    dec.run_eager(args.warmup)
     torch.cuda.synchronize()
 
     # ---- eager (host-launched) throughput, for reference ----
     n_eager = min(args.steps, 500)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(n_eager):
-        run_step(args.warmup + i)
+    dec.run_eager(n_eager)
     e1.record()
     torch.cuda.synchronize()
     eager_ms_per_step = e0.elapsed_time(e1) / n_eager
 
-    # ---- HIP graph of G steps (two per layer, so the double-buffered
-    # generated-token counts of the fused steps return to their buffers) ----
-    G = 2 * len(layers)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(G):
-            run_step(i)
+    # ---- HIP graphs: G = 2 L steps (two per layer), and a tail for K mod G ----
+    G = dec.G
+    graph = dec.capture()
     graph.replay()
     torch.cuda.synchronize()
     reps, rest = divmod(args.steps, G)
     tail = None
-    if rest:   # the last K mod G steps, one step on each of the first layers
-        tail = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(tail):
-            for i in range(rest):
-                run_step(i)
+    if rest:
+        tail = dec.capture(rest)
         tail.replay()
         torch.cuda.synchronize()
+        dec.fix_tail_counts(rest)
     steps = reps * G + rest
 
     # ---- timed region: exactly K steps ----
@@ -597,8 +710,8 @@ def main():
               for _ in range(nk)]
         torch.cuda.synchronize()
         for i in range(nk):
-            s = layers[i % len(layers)]
-            q, k, v = pool[i % pool_n]
+            s = dec.layers[i % dec.L]
+            q, k, v = dec.q[i % G], dec.k[i % G], dec.v[i % G]
             calls = [lambda: s.append(k, v)]
             if w.sparse:
                 calls += [lambda: s.score(q), s.select, lambda: s.attend(q)]
@@ -614,16 +727,18 @@ def main():
 
     live = None
     if w.sparse:
-        sb = base.sel_bias.cpu().numpy()
-        si = base.sel_idx.cpu().numpy()
-        live = int(np.sum((si >= 0) & np.isfinite(sb)))
+        if fused:   # the selections of the last replay's steps
+            slots = range(min(steps, G))
+            live = sum(dec.live_blocks(g) for g in slots) / len(slots)
+        else:
+            sb, si = dec.layers[0].sel_bias.cpu().numpy(), dec.layers[0].sel_idx.cpu().numpy()
+            live = int(np.sum((si >= 0) & np.isfinite(sb)))
     abytes = algorithmic_bytes(w, live)
     if fused:   # the step kernel moves what the rows it fuses move (scores stay on chip)
-        rows = dict(abytes)
-        total = sum(rows.values())
+        total = sum(abytes.values())
         if w.sparse:
             total -= 2 * w.units * w.n_blocks * 4
-        abytes = {names[0]: total}
+        abytes = {names[0]: int(total)}
     kernels = {n: {"avg_us": round(kern_ms[n] * 1e3, 3), "algorithmic_bytes": abytes[n],
                    "gbs": round(abytes[n] / (kern_ms[n] * 1e-3) / 1e9, 1)} for n in names}
     dom = max(names, key=lambda n: kern_ms[n])
@@ -638,7 +753,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "prefix_tokens": w.prefix_len, "pages": w.pages, "window": w.window, "t0": w.t0,
                    "sparse": w.sparse, "topk": w.topk if w.sparse else None,
-                   "block": w.block if w.sparse else None, "layers_cycled": len(layers),
+                   "block": w.block if w.sparse else None, "layers_cycled": dec.L,
                    "splits": ((args.num_splits or 8) if w.sparse and fused
                               else U.uocr_srswa_splits(base.shape, base.route, args.num_splits) if w.sparse
                               else U.uocr_rswa_splits(base.shape, args.num_splits)),
@@ -648,8 +763,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic(dom, w.name)},
         "step_gbs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "timing": (f"HIP graph of {G} steps replayed {reps} times" + (f" + {rest} steps" if rest else "")
-                   + f"; eager launches: {eager_ms_per_step * 1e3:.2f} us/step"),
+        "timing": (f"HIP graph of {G} steps replayed {reps} times" + (f" + a {rest}-step graph" if rest else "")
+                   + f" between HIP events; eager launches: {eager_ms_per_step * 1e3:.2f} us/step"),
         "eager_ms_per_step": round(eager_ms_per_step, 5),
         "kernels": kernels,
         "kernel_source": kernel_source_hash(),
@@ -658,14 +773,9 @@ def main():
         result["routing"] = {"live_blocks_per_unit": round(live / w.units, 3),
                              "index_build_ms_per_layer": round(idx_ms, 4),
                              "index_build_gbs": round(index_bytes(w) / (idx_ms * 1e-3) / 1e9, 1)}
-        # the same step time priced as if every selected block were read (the
-        # achieved figure above counts only blocks with p > 0, the ones read)
-        full = sum(algorithmic_bytes(w, None).values()) - (2 * w.units * w.n_blocks * 4 if fused else 0)
-        result["routing"]["all_selected_blocks_bytes"] = full
-        result["routing"]["all_selected_blocks_gbs"] = round(full / (ms_per_step * 1e-3) / 1e9, 1)
     result["setup_s"] = round(setup_s, 1)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

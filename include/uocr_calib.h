@@ -1,0 +1,55 @@
+/*
+ * uocr_calib.h -- measurement kernels of libuocr.so (gfx950).
+ *
+ * These calls are not part of the method: they give the denominators the
+ * decode kernels are measured against on the machine at hand, so that the
+ * figures quoted for them can be reproduced from the library alone.
+ *   - uocr_calib_read: the read bandwidth a plain streaming kernel reaches
+ *     over a large buffer, with ordinary or nontemporal 16-byte loads (the
+ *     "attainable" HBM rate next to the published 8 TB/s peak);
+ *   - uocr_calib_empty: a launch that does nothing, the floor of any kernel
+ *     in a HIP graph at a given grid;
+ *   - uocr_calib_pull: each of `groups` workgroups reads its own contiguous
+ *     run of bytes_per_group bytes and nothing else, the time one compute
+ *     unit needs to bring in a given amount of data when only some units of
+ *     the chip are busy (the floor of a step whose units each read that much).
+ *
+ * Conventions as in uocr.h: device pointers, the caller owns every buffer,
+ * stream is a hipStream_t passed as void* (NULL = default stream), the call
+ * returns once the work is enqueued, 0 on success and a negative uocr_status
+ * on failure.  src must be 16-byte aligned;
+ * `sink` receives at most one word per workgroup and only if the data hash to
+ * a value no real buffer produces, so that the loads cannot be dropped; it
+ * needs room for one uint32 per workgroup.
+ */
+#ifndef UOCR_CALIB_H
+#define UOCR_CALIB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` (a multiple of 16, > 0) from src with one grid of 4096
+ * workgroups x 256 threads, each streaming its own contiguous 1/4096 of the
+ * buffer; nontemporal != 0 uses nontemporal loads.  sink: 4096 uint32.     */
+int uocr_calib_read(const void* src, size_t bytes, int32_t nontemporal, uint32_t* sink, void* stream);
+
+/* An empty kernel of `groups` workgroups of `threads` threads
+ * (1 <= groups <= 2^20, threads in {64, 128, 256, 512, 1024}).             */
+int uocr_calib_empty(int32_t groups, int32_t threads, void* stream);
+
+/* Workgroup g (0 <= g < groups) reads bytes [g * bytes_per_group,
+ * (g + 1) * bytes_per_group) of src with `threads` threads, 16 bytes per
+ * load, up to 8 loads per thread in flight.  bytes_per_group a multiple of
+ * 16 in [16, 2^26]; groups and threads as for uocr_calib_empty; src must hold
+ * groups * bytes_per_group bytes.  sink: `groups` uint32.                   */
+int uocr_calib_pull(const void* src, size_t bytes_per_group, int32_t groups, int32_t threads,
+                    int32_t nontemporal, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UOCR_CALIB_H */

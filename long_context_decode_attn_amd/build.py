@@ -2,7 +2,7 @@
 
     python -m long_context_decode_attn_amd.build
 
-compiles csrc/uocr_kernels.hip and csrc/uocr_api.cpp into
+compiles csrc/uocr_kernels.hip, csrc/uocr_api.cpp and csrc/uocr_calib.hip into
 long_context_decode_attn_amd/libuocr.so.  Packed fp32 instructions are
 switched off for all device code.
 """
@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libuocr.so")
-SOURCES = [os.path.join(CSRC, "uocr_kernels.hip"), os.path.join(CSRC, "uocr_api.cpp")]
+SOURCES = [os.path.join(CSRC, "uocr_kernels.hip"), os.path.join(CSRC, "uocr_api.cpp"),
+           os.path.join(CSRC, "uocr_calib.hip")]
 
 ARCH = "gfx950"
 
@@ -48,15 +49,18 @@ def build_library(verbose: bool = True) -> str:
     cc = hipcc()
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+    objs, procs = [], []
+    for src in SOURCES:   # the sources compile in parallel
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmd = [cc, *compile_flags(), *lang, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
         objs.append(obj)
+    for cmd, p in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(p.returncode, cmd)
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

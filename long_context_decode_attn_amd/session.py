@@ -114,17 +114,19 @@ class DecodeSession:
             U.uocr_rswa_decode(self.shape, q, self.k_prefix, self.v_prefix, self.prefix_len, self.k_ring,
                                self.v_ring, self.t_gen, self.out, self.workspace, self.num_splits)
 
-    def fused_step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+    def fused_step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out=None, sel=None) -> None:
         """The whole step in one launch; the generated-token counts move to
-        the other buffer, which becomes `t_gen`."""
+        the other buffer, which becomes `t_gen`.  out (and, for SR-SWA, sel =
+        (idx, prob, bias)) default to the session's own buffers."""
+        out = self.out if out is None else out
         if self.w.sparse:
+            si, sp, sb = (self.sel_idx, self.sel_prob, self.sel_bias) if sel is None else sel
             U.uocr_srswa_step(self.shape, self.route, q, k_new, v_new, self.k_prefix, self.v_prefix,
                               self.prefix_len, self.proj, self.kbar, self.k_ring, self.v_ring, self.t_gen,
-                              self.t_gen_next, self.sel_idx, self.sel_prob, self.sel_bias, self.out,
-                              self.num_splits)
+                              self.t_gen_next, si, sp, sb, out, self.num_splits)
         else:
             U.uocr_rswa_step(self.shape, q, k_new, v_new, self.k_prefix, self.v_prefix, self.prefix_len,
-                             self.k_ring, self.v_ring, self.t_gen, self.t_gen_next, self.out, self.workspace,
+                             self.k_ring, self.v_ring, self.t_gen, self.t_gen_next, out, self.workspace,
                              self.num_splits)
         self.t_gen, self.t_gen_next = self.t_gen_next, self.t_gen
 

@@ -51,7 +51,9 @@ class Workload:
     topk: int = 16
     planted: int = 0      # planted relevant blocks per sequence
     planted_on_pages: bool = False   # one planted block per distinct page
+    planted_noise: float = 1.0       # scale of the N(0, 1) part of planted keys
     fixed_query: bool = False        # same query every step (the planted q*)
+    query_noise: bool = False        # with fixed_query: (q* + xi_t) / sqrt(2), xi_t ~ N(0, I) per step
 
     @property
     def prefix_len(self) -> int:
@@ -105,6 +107,25 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("srswa-125p-b8", batch=8, heads=10, head_dim=128, dtype="bf16",
                  pages=125, prompt=0, t0=128, steps=2048, seed=1005, sparse=True,
                  planted=24, planted_on_pages=True, fixed_query=True),
+        # the same two shapes with a per-step query (q* + xi_t) / sqrt(2), so
+        # that the routing decision changes from step to step
+        Workload("srswa-40p-b32-qnoise", batch=32, heads=10, head_dim=128, dtype="bf16",
+                 pages=40, prompt=0, t0=128, steps=1000, seed=1004, sparse=True,
+                 planted=16, fixed_query=True, query_noise=True),
+        Workload("srswa-125p-b8-qnoise", batch=8, heads=10, head_dim=128, dtype="bf16",
+                 pages=125, prompt=0, t0=128, steps=2048, seed=1005, sparse=True,
+                 planted=24, planted_on_pages=True, fixed_query=True, query_noise=True),
+        # wide routing: the planted blocks' own N(0, 1) part is scaled by 0.02,
+        # so their scores lie within a fraction of each other and the 1.5-entmax
+        # support holds every planted block (16 at 40 pages; 24 at 125 pages, of
+        # which the top 16 are selected): each query reads 16 blocks, the
+        # working set of about 16 x 32 reference tokens the pages describe
+        Workload("srswa-40p-b32-wide", batch=32, heads=10, head_dim=128, dtype="bf16",
+                 pages=40, prompt=0, t0=128, steps=1000, seed=1008, sparse=True,
+                 planted=16, planted_noise=0.02, fixed_query=True),
+        Workload("srswa-125p-b8-wide", batch=8, heads=10, head_dim=128, dtype="bf16",
+                 pages=125, prompt=0, t0=128, steps=2048, seed=1009, sparse=True,
+                 planted=24, planted_on_pages=True, planted_noise=0.02, fixed_query=True),
     ]
 }
 
@@ -196,6 +217,8 @@ def prefix_kv_seq(w: Workload, b: int, m_cap: Optional[int] = None):
         qs = fixed_query_f32(w, b)
         for blk in planted_blocks(w, b):
             lo, hi = blk * w.block, min(blk * w.block + w.block, m)
+            if w.planted_noise != 1.0:
+                k[:, lo:hi, :] *= np.float32(w.planted_noise)
             k[:, lo:hi, :] += np.float32(0.5) * qs[:, None, :]
     ks, vs = store(k, w.dtype), store(v, w.dtype)
     if m_cap > m:
@@ -229,9 +252,14 @@ def history_token(w: Workload, tau: int):
 
 
 def step_query(w: Workload, step: int) -> np.ndarray:
-    """Query of decode step `step` (0-based), storage array [B][H][D]."""
+    """Query of decode step `step` (0-based), storage array [B][H][D]: the
+    planted q* (fixed_query), (q* + xi_t) / sqrt(2) with xi_t ~ N(0, I) drawn
+    per step (fixed_query and query_noise), or N(0, 1)."""
     if w.fixed_query:
         q = np.stack([fixed_query_f32(w, b) for b in range(w.batch)]).astype(np.float32)
+        if w.query_noise:
+            xi = normal32(w.seed, (w.batch, w.heads, w.head_dim), _S_Q, step)
+            q = ((q + xi) * np.float32(1.0 / math.sqrt(2.0))).astype(np.float32)
         return store(q, w.dtype)
     return store(normal32(w.seed, (w.batch, w.heads, w.head_dim), _S_Q, step), w.dtype)
 

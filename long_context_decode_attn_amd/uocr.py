@@ -125,6 +125,9 @@ def load_library():
         "uocr_rswa_step": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P]),
         "uocr_srswa_step": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _P, _I32, _P]),
+        "uocr_calib_read": (ctypes.c_int, [_P, _SZ, _I32, _P, _P]),
+        "uocr_calib_empty": (ctypes.c_int, [_I32, _I32, _P]),
+        "uocr_calib_pull": (ctypes.c_int, [_P, _SZ, _I32, _I32, _I32, _P, _P]),
         "uocr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "uocr_last_error": (ctypes.c_char_p, []),
         "uocr_version": (ctypes.c_int, []),
@@ -141,7 +144,8 @@ EXPORTED = ("uocr_ring_append", "uocr_rswa_splits", "uocr_rswa_workspace_bytes",
             "uocr_rswa_decode", "uocr_block_index_build", "uocr_block_index_range", "uocr_block_score", "uocr_entmax15_topk",
             "uocr_prefill_route", "uocr_ngram_ban", "uocr_rope_page2d",
             "uocr_srswa_splits", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
-            "uocr_status_string", "uocr_last_error", "uocr_version")
+            "uocr_status_string", "uocr_last_error", "uocr_version",
+            "uocr_calib_read", "uocr_calib_empty", "uocr_calib_pull")
 
 
 # ----------------------------------------------------------------------------
@@ -381,6 +385,35 @@ def uocr_srswa_step(shape: Shape, route: Route, q, k_new, v_new, k_prefix, v_pre
           _ptr(k_prefix), _ptr(v_prefix), _ptr(prefix_len), _ptr(proj), _ptr(kbar_idx), _ptr(k_ring), _ptr(v_ring),
           _ptr(t_gen_in), _ptr(t_gen_out), _ptr(sel_idx), _ptr(sel_prob), _ptr(sel_bias), _ptr(out), num_splits,
           _stream(stream))
+
+
+# ----------------------------------------------------------------------------
+# measurement kernels (include/uocr_calib.h)
+# ----------------------------------------------------------------------------
+def _calib_call(fn: str, *args) -> None:
+    rc = getattr(load_library(), fn)(*args)
+    if rc != 0:
+        raise UocrError(fn, rc, STATUS.get(rc, str(rc)))
+
+
+def uocr_calib_read(src: torch.Tensor, nontemporal: bool, sink: torch.Tensor, stream=None) -> None:
+    """Stream the whole of src (a device tensor, size a multiple of 16 bytes)."""
+    _check(sink, "sink", torch.int32, (4096,))
+    _calib_call("uocr_calib_read", _ptr(src), src.numel() * src.element_size(), int(nontemporal), _ptr(sink),
+                _stream(stream))
+
+
+def uocr_calib_empty(groups: int, threads: int, stream=None) -> None:
+    _calib_call("uocr_calib_empty", groups, threads, _stream(stream))
+
+
+def uocr_calib_pull(src: torch.Tensor, bytes_per_group: int, groups: int, threads: int, nontemporal: bool,
+                    sink: torch.Tensor, stream=None) -> None:
+    if src.numel() * src.element_size() < bytes_per_group * groups:
+        raise ValueError("src is smaller than groups x bytes_per_group")
+    _check(sink, "sink", torch.int32, (groups,))
+    _calib_call("uocr_calib_pull", _ptr(src), bytes_per_group, groups, threads, int(nontemporal), _ptr(sink),
+                _stream(stream))
 
 
 def uocr_version() -> int:

@@ -19,9 +19,14 @@ def _lib():
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "uocr.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(uocr_[a-z0-9_]+)\s*\(", src)))
+    """Every function name declared in include/*.h."""
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(uocr_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
@@ -203,3 +208,4 @@ def test_product_path_has_no_oracle_or_fallback():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "uocr_oracle" not in text, f
+
