@@ -39,8 +39,9 @@
  *     prefix_len[b] to [0, prefix_cap], t_gen[b] below 0 to 0, sel_idx
  *     entries outside [0, ceil(prefix_len[b]/block_size)) are skipped.
  *   - Ownership: the caller allocates and owns every buffer; the library
- *     allocates nothing, keeps no state except a thread-local error string,
- *     never synchronises the stream, and returns as soon as the work is
+ *     allocates nothing and keeps no state except a thread-local error string
+ *     (and, for uocr_rswa_decode_static, a static device workspace per GPU
+ *     and its address), never synchronises the stream, and returns as soon as the work is
  *     enqueued on `stream` (a hipStream_t passed as void*; NULL = default
  *     stream).
  *   - Errors: every call validates its arguments on the host before any
@@ -138,6 +139,29 @@ int uocr_rswa_decode(const uocr_shape* shape, const void* q,
                      const void* v_ring, const int32_t* t_gen, void* out,
                      void* workspace, size_t ws_bytes, int32_t num_splits,
                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * uocr_rswa_decode_static -- uocr_rswa_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * hosts that forbid allocation): the split partials go to a workspace of
+ * 16 MiB that the library keeps in a static device array, one per GPU, held
+ * until the process ends.  Nothing is allocated and no workspace is passed.
+ *   Arguments, layouts and results as for uocr_rswa_decode with the same
+ *   num_splits (the same kernels run).  num_splits = 0 picks the split count
+ *   of uocr_rswa_decode, reduced if need be until the partials fit in 16 MiB;
+ *   an explicit num_splits whose partials need more returns
+ *   UOCR_ERR_WORKSPACE before anything is launched.  The first call on a
+ *   device looks up that device's copy of the array (with the device
+ *   current); a failure there returns UOCR_ERR_HIP.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (concurrent streams, or host threads) race and must be
+ *   serialised by the caller.  The array needs no clearing: each split
+ *   writes its partial before the merge reads it.                           */
+int uocr_rswa_decode_static(const uocr_shape* shape, const void* q,
+                            const void* k_prefix, const void* v_prefix,
+                            const int32_t* prefix_len, const void* k_ring,
+                            const void* v_ring, const int32_t* t_gen, void* out,
+                            int32_t num_splits, void* stream);
 
 /* ---------------------------------------------------------------------------
  * uocr_block_index_build -- block keys of the prefix, once after prefill.

@@ -7,9 +7,16 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "uocr_internal.h"
+
+// Static workspace of uocr_rswa_decode_static (see static_scratch below).
+namespace {
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+}
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -158,6 +165,19 @@ int srswa_waves(const uocr_route* r, int32_t req) {
   return W;
 }
 
+// ---------------------------------------------------------------------------
+// Static workspace of uocr_rswa_decode_static: a file-scope device array.
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` only stands for the array; its address on a device
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int static_scratch(const char* fn, void** ptr);
+
 int block_index(const char* fn, const uocr_shape* shape, const uocr_route* route, const void* k_prefix,
                 const int32_t* prefix_len, const float* proj, float* kbar_idx, int32_t first_block,
                 int32_t last_block, void* stream) {
@@ -179,6 +199,104 @@ int block_index(const char* fn, const uocr_shape* shape, const uocr_route* route
                     shape->heads, shape->prefix_cap, nb_cap, first_block, last_block - first_block};
   return hip_status(uocr::launch_block_index(shape->dtype, shape->head_dim, a,
                                              static_cast<hipStream_t>(stream)), fn);
+}
+
+// Dense decode of both entry points: the caller's workspace, or (use_static)
+// the library's static one.
+int rswa_decode_impl(const char* fn, const uocr_shape* shape, const void* q, const void* k_prefix,
+                     const void* v_prefix, const int32_t* prefix_len, const void* k_ring,
+                     const void* v_ring, const int32_t* t_gen, void* out, void* workspace,
+                     size_t ws_bytes, int32_t num_splits, bool use_static, void* stream) {
+  CHECK(check_shape(shape, fn));
+  NEED(q, "q");
+  NEED(k_ring, "k_ring");
+  NEED(v_ring, "v_ring");
+  NEED(t_gen, "t_gen");
+  NEED(prefix_len, "prefix_len");
+  NEED(out, "out");
+  if (shape->prefix_cap > 0) {
+    NEED(k_prefix, "k_prefix");
+    NEED(v_prefix, "v_prefix");
+    ALIGN16(k_prefix, "k_prefix");
+    ALIGN16(v_prefix, "v_prefix");
+  }
+  ALIGN16(q, "q");
+  ALIGN16(k_ring, "k_ring");
+  ALIGN16(v_ring, "v_ring");
+  ALIGN16(out, "out");
+  ALIGN4(t_gen, "t_gen");
+  ALIGN4(prefix_len, "prefix_len");
+  if (num_splits < 0) return fail(UOCR_ERR_SHAPE, "%s: num_splits %d < 0", fn, num_splits);
+  int S, C;
+  rswa_geometry(shape, num_splits, &S, &C);
+  const int units = units_of(shape);
+  size_t need = ws_bytes_for(units, S, shape->head_dim);
+  if (use_static && need > kStaticScratchBytes) {
+    if (num_splits > 0)
+      return fail(UOCR_ERR_WORKSPACE,
+                  "%s: %d splits of %d units need a workspace of %zu bytes, above the static %zu bytes; "
+                  "ask for fewer splits (0 picks a count that fits)", fn, S, units, need, kStaticScratchBytes);
+    // the chosen geometry does not fit: the most splits whose partials fit
+    int s_fit = S;
+    while (s_fit > 1 && ws_bytes_for(units, s_fit, shape->head_dim) > kStaticScratchBytes) --s_fit;
+    rswa_geometry(shape, s_fit, &S, &C);
+    need = ws_bytes_for(units, S, shape->head_dim);
+  }
+  if (need > 0) {
+    if (use_static) {
+      CHECK(static_scratch(fn, &workspace));
+      ws_bytes = kStaticScratchBytes;
+    }
+    NEED(workspace, "workspace");
+    ALIGN16(workspace, "workspace");
+    if (ws_bytes < need)
+      return fail(UOCR_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+  }
+  uocr::DecodeArgs a{};
+  a.q = q;
+  a.k_prefix = k_prefix;
+  a.v_prefix = v_prefix;
+  a.prefix_len = prefix_len;
+  a.k_ring = k_ring;
+  a.v_ring = v_ring;
+  a.t_gen = t_gen;
+  a.out = out;
+  if (need > 0) {
+    a.part_ml = static_cast<float*>(workspace);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)units * S * 2 * 4));
+  }
+  a.units = units;
+  a.heads = shape->heads;
+  a.prefix_cap = shape->prefix_cap;
+  a.window = shape->window;
+  a.splits = S;
+  a.chunk = C;
+  a.waves = kDenseWaves;
+  a.qscale = shape->scale * 1.4426950408889634f;
+  return hip_status(uocr::launch_rswa_decode(shape->dtype, shape->head_dim, a,
+                                             static_cast<hipStream_t>(stream)), fn);
+}
+
+// Address of this device's copy of `scratch`, taken on the first call on
+// the device (with it current) and kept.
+int static_scratch(const char* fn, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(UOCR_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(UOCR_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library keeps addresses for", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(UOCR_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return UOCR_OK;
 }
 
 }  // namespace
@@ -240,60 +358,16 @@ int uocr_rswa_decode(const uocr_shape* shape, const void* q, const void* k_prefi
                      const void* v_prefix, const int32_t* prefix_len, const void* k_ring,
                      const void* v_ring, const int32_t* t_gen, void* out, void* workspace,
                      size_t ws_bytes, int32_t num_splits, void* stream) {
-  const char* fn = "uocr_rswa_decode";
-  CHECK(check_shape(shape, fn));
-  NEED(q, "q");
-  NEED(k_ring, "k_ring");
-  NEED(v_ring, "v_ring");
-  NEED(t_gen, "t_gen");
-  NEED(prefix_len, "prefix_len");
-  NEED(out, "out");
-  if (shape->prefix_cap > 0) {
-    NEED(k_prefix, "k_prefix");
-    NEED(v_prefix, "v_prefix");
-    ALIGN16(k_prefix, "k_prefix");
-    ALIGN16(v_prefix, "v_prefix");
-  }
-  ALIGN16(q, "q");
-  ALIGN16(k_ring, "k_ring");
-  ALIGN16(v_ring, "v_ring");
-  ALIGN16(out, "out");
-  ALIGN4(t_gen, "t_gen");
-  ALIGN4(prefix_len, "prefix_len");
-  if (num_splits < 0) return fail(UOCR_ERR_SHAPE, "%s: num_splits %d < 0", fn, num_splits);
-  int S, C;
-  rswa_geometry(shape, num_splits, &S, &C);
-  const int units = units_of(shape);
-  const size_t need = ws_bytes_for(units, S, shape->head_dim);
-  if (need > 0) {
-    NEED(workspace, "workspace");
-    ALIGN16(workspace, "workspace");
-    if (ws_bytes < need)
-      return fail(UOCR_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
-  }
-  uocr::DecodeArgs a{};
-  a.q = q;
-  a.k_prefix = k_prefix;
-  a.v_prefix = v_prefix;
-  a.prefix_len = prefix_len;
-  a.k_ring = k_ring;
-  a.v_ring = v_ring;
-  a.t_gen = t_gen;
-  a.out = out;
-  if (need > 0) {
-    a.part_ml = static_cast<float*>(workspace);
-    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)units * S * 2 * 4));
-  }
-  a.units = units;
-  a.heads = shape->heads;
-  a.prefix_cap = shape->prefix_cap;
-  a.window = shape->window;
-  a.splits = S;
-  a.chunk = C;
-  a.waves = kDenseWaves;
-  a.qscale = shape->scale * 1.4426950408889634f;
-  return hip_status(uocr::launch_rswa_decode(shape->dtype, shape->head_dim, a,
-                                             static_cast<hipStream_t>(stream)), fn);
+  return rswa_decode_impl("uocr_rswa_decode", shape, q, k_prefix, v_prefix, prefix_len, k_ring, v_ring, t_gen,
+                          out, workspace, ws_bytes, num_splits, false, stream);
+}
+
+int uocr_rswa_decode_static(const uocr_shape* shape, const void* q, const void* k_prefix,
+                            const void* v_prefix, const int32_t* prefix_len, const void* k_ring,
+                            const void* v_ring, const int32_t* t_gen, void* out, int32_t num_splits,
+                            void* stream) {
+  return rswa_decode_impl("uocr_rswa_decode_static", shape, q, k_prefix, v_prefix, prefix_len, k_ring, v_ring,
+                          t_gen, out, nullptr, 0, num_splits, true, stream);
 }
 
 int uocr_block_index_build(const uocr_shape* shape, const uocr_route* route, const void* k_prefix,

@@ -112,6 +112,7 @@ def load_library():
         "uocr_rswa_splits": (_I32, [SP, _I32]),
         "uocr_rswa_workspace_bytes": (_SZ, [SP, _I32]),
         "uocr_rswa_decode": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P]),
+        "uocr_rswa_decode_static": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
         "uocr_block_index_build": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P]),
         "uocr_block_index_range": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _I32, _I32, _P]),
         "uocr_block_score": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P]),
@@ -141,7 +142,7 @@ def load_library():
 
 
 EXPORTED = ("uocr_ring_append", "uocr_rswa_splits", "uocr_rswa_workspace_bytes",
-            "uocr_rswa_decode", "uocr_block_index_build", "uocr_block_index_range", "uocr_block_score", "uocr_entmax15_topk",
+            "uocr_rswa_decode", "uocr_rswa_decode_static", "uocr_block_index_build", "uocr_block_index_range", "uocr_block_score", "uocr_entmax15_topk",
             "uocr_prefill_route", "uocr_ngram_ban", "uocr_rope_page2d",
             "uocr_srswa_splits", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
             "uocr_status_string", "uocr_last_error", "uocr_version",
@@ -236,6 +237,22 @@ def uocr_rswa_decode(shape: Shape, q, k_prefix, v_prefix, prefix_len, k_ring, v_
     wp, wb = _ws(workspace)
     _call("uocr_rswa_decode", ctypes.byref(shape.c()), _ptr(q), _ptr(k_prefix), _ptr(v_prefix), _ptr(prefix_len),
           _ptr(k_ring), _ptr(v_ring), _ptr(t_gen), _ptr(out), wp, wb, num_splits, _stream(stream))
+
+
+def uocr_rswa_decode_static(shape: Shape, q, k_prefix, v_prefix, prefix_len, k_ring, v_ring, t_gen, out,
+                            num_splits: int = 0, stream=None) -> None:
+    """uocr_rswa_decode with the library's static workspace (no workspace argument)."""
+    B, H, D, n, m, dt = shape.batch, shape.heads, shape.head_dim, shape.window, shape.prefix_cap, shape.torch_dtype
+    _check(q, "q", dt, (B, H, D))
+    _check(k_prefix, "k_prefix", dt, (B, H, m, D))
+    _check(v_prefix, "v_prefix", dt, (B, H, m, D))
+    _check(prefix_len, "prefix_len", torch.int32, (B,))
+    _check(k_ring, "k_ring", dt, (B, H, n, D))
+    _check(v_ring, "v_ring", dt, (B, H, n, D))
+    _check(t_gen, "t_gen", torch.int32, (B,))
+    _check(out, "out", dt, (B, H, D))
+    _call("uocr_rswa_decode_static", ctypes.byref(shape.c()), _ptr(q), _ptr(k_prefix), _ptr(v_prefix),
+          _ptr(prefix_len), _ptr(k_ring), _ptr(v_ring), _ptr(t_gen), _ptr(out), num_splits, _stream(stream))
 
 
 def uocr_block_index_build(shape: Shape, route: Route, k_prefix, prefix_len, proj, kbar_idx, stream=None) -> None:

@@ -209,3 +209,17 @@ def test_product_path_has_no_oracle_or_fallback():
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "uocr_oracle" not in text, f
 
+
+def test_static_workspace_refuses_a_split_count_that_does_not_fit():
+    """uocr_rswa_decode_static: an explicit split count whose partials exceed
+    the library's static workspace is refused before anything is launched."""
+    U, lib = _lib()
+    sh = U._Shape(1 << 14, 64, 128, 1 << 17, 128, 1, 0.088)   # 2^20 units x 16 splits: 8 GiB of partials
+    rc = lib.uocr_rswa_decode_static(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert rc == -4, rc
+    assert "static" in lib.uocr_last_error().decode()
+    # invalid arguments are refused as by uocr_rswa_decode
+    assert lib.uocr_rswa_decode_static(ctypes.byref(_shape(U)), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                       None) == -1
+    assert lib.uocr_rswa_decode_static(ctypes.byref(_shape(U)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1,
+                                       None) == -2
