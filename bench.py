@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--rope-page2d", type=int, default=0, metavar="TQ",
                     help="instead of the decode step, time uocr_rope_page2d over the keys of a prefill chunk of TQ "
                          "tokens per (sequence, head) of the workload (page_mod 2, base 10000)")
+    ap.add_argument("--rope", action="store_true",
+                    help="fuse the page2d rotary embedding of q and k_new into the step kernels")
     ap.add_argument("--calibrate", action="store_true",
                     help="instead of the decode step, measure the denominators: plain and nontemporal read "
                          "streams over 2 GiB, empty launches and per-workgroup pulls")
@@ -637,7 +639,7 @@ def main():
         del probe
     est_bytes = sum(algorithmic_bytes(w, live_est).values())
     n_layers = args.layers if args.layers > 0 else layers_for(est_bytes)
-    dec = LayeredDecoder(w, n_layers, num_splits=args.num_splits, fused=fused, base=base)
+    dec = LayeredDecoder(w, n_layers, num_splits=args.num_splits, fused=fused, base=base, rope=args.rope)
     torch.cuda.synchronize()
 
     # one-time block index per layer (timed on its own, reported separately)
@@ -757,7 +759,8 @@ def main():
                    "splits": ((args.num_splits or 8) if w.sparse and fused
                               else U.uocr_srswa_splits(base.shape, base.route, args.num_splits) if w.sparse
                               else U.uocr_rswa_splits(base.shape, args.num_splits)),
-                   "mode": args.mode, "accumulate": "f32 attention, f64 routing",
+                   "mode": args.mode, "rope": "page2d fused" if args.rope else None,
+                   "accumulate": "f32 attention, f64 routing",
                    "parallelism": "single-gpu"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -305,15 +305,27 @@ int uocr_rope_page2d(const uocr_shape* shape, void* x, void* y, int32_t tokens,
  *   bias sel_bias[i] added to the scaled logit of each of its tokens, plus
  *   the visible window with bias 0; out = softmax-weighted sum of values.
  *   sel_bias NULL means bias 0 for every selected block.  A block whose bias
- *   is -inf has weight exactly 0 and is not read at all.  One workgroup per
- *   unit; num_splits = waves per workgroup (0 = default 8, at most 8).    */
+ *   is -inf has weight exactly 0 and is not read at all.
+ *   A unit's live blocks and window rows are shared among num_splits
+ *   workgroups (0 = one per unit when there are at least 256 units, else
+ *   enough for about 256 workgroups, at most 8 per unit; uocr_srswa_splits
+ *   gives the count); with more than one, each leaves its (max, sum, partial
+ *   output) in the workspace and a second kernel in the same stream merges
+ *   them, as in uocr_rswa_decode.  Size the workspace with
+ *   uocr_srswa_workspace_bytes for the same num_splits (0 bytes for one
+ *   workgroup per unit: then workspace may be NULL); no initialisation is
+ *   needed; calls that overlap on one workspace race.  Beyond the call
+ *   list of the measurement plan, num_splits lets a caller fix the split
+ *   count, as for the dense decode.                                         */
 int32_t uocr_srswa_splits(const uocr_shape* shape, const uocr_route* route, int32_t num_splits);
+size_t uocr_srswa_workspace_bytes(const uocr_shape* shape, const uocr_route* route, int32_t num_splits);
 int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route,
                       const void* q, const void* k_prefix, const void* v_prefix,
                       const int32_t* prefix_len, const int32_t* sel_idx,
                       const float* sel_bias, const void* k_ring,
                       const void* v_ring, const int32_t* t_gen, void* out,
-                      int32_t num_splits, void* stream);
+                      void* workspace, size_t ws_bytes, int32_t num_splits,
+                      void* stream);
 
 /* ---------------------------------------------------------------------------
  * Fused decode steps: one call = one whole decode step of the path above.
@@ -330,13 +342,31 @@ int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route,
  * sparse step keeps the block scores on chip (no scores array).
  *   uocr_rswa_step: workspace and num_splits as for uocr_rswa_decode.
  *   uocr_srswa_step: one workgroup per unit; num_splits = waves per
- *   workgroup, 4, 8 or 16 (0 = 8).                                         */
+ *   workgroup, 4, 8 or 16 (0 = 8).
+ *
+ * rope (NULL: none) fuses the page2d rotary embedding of uocr_rope_page2d
+ * into the step.  [nxmr.cn/news/162408, section "2D 位置编码"; the rotation
+ * and its readings as for uocr_rope_page2d.]  The step's new token of
+ * sequence b sits at (rope->page[b], rope->offset[b]) ([B] int32, device,
+ * 4-byte aligned); q and k_new are turned by that position before anything
+ * reads them: the turned k row is what enters the ring, and the turned q is
+ * both the routing query and the attention query.  q and k_new themselves
+ * are left unchanged.  The results are those of uocr_rope_page2d on q and
+ * k_new (x = q, y = k_new, tokens = 1) followed by the step without rope,
+ * bit for bit.  page_mod >= 0 and base finite and > 0, else UOCR_ERR_SHAPE. */
+typedef struct {
+  const int32_t* page;
+  const int32_t* offset;
+  int32_t page_mod;
+  float base;
+} uocr_rope;
+
 int uocr_rswa_step(const uocr_shape* shape, const void* q, const void* k_new,
                    const void* v_new, const void* k_prefix, const void* v_prefix,
                    const int32_t* prefix_len, void* k_ring, void* v_ring,
                    const int32_t* t_gen_in, int32_t* t_gen_out, void* out,
                    void* workspace, size_t ws_bytes, int32_t num_splits,
-                   void* stream);
+                   const uocr_rope* rope, void* stream);
 int uocr_srswa_step(const uocr_shape* shape, const uocr_route* route,
                     const void* q, const void* k_new, const void* v_new,
                     const void* k_prefix, const void* v_prefix,
@@ -344,7 +374,8 @@ int uocr_srswa_step(const uocr_shape* shape, const uocr_route* route,
                     const float* kbar_idx, void* k_ring, void* v_ring,
                     const int32_t* t_gen_in, int32_t* t_gen_out,
                     int32_t* sel_idx, float* sel_prob, float* sel_bias,
-                    void* out, int32_t num_splits, void* stream);
+                    void* out, int32_t num_splits, const uocr_rope* rope,
+                    void* stream);
 
 /* ---------------------------------------------------------------------------
  * Diagnostics. */

@@ -115,7 +115,7 @@ size_t ws_bytes_for(int units, int splits, int head_dim) {
 }
 
 constexpr int kDenseWaves = 4;    // waves per workgroup of the dense decode
-constexpr int kSparseWaves = 8;   // default waves per unit of the sparse decode
+constexpr int kSparseWaves = 8;   // waves per workgroup of the sparse decode and step (default)
 constexpr int kCUs = 256;         // compute units of an MI355X
 constexpr int kMaxPrefillQueries = 1 << 20;  // queries per unit in one prefill routing call
 
@@ -155,14 +155,16 @@ void rswa_geometry(const uocr_shape* sh, int32_t req, int* splits, int* chunk) {
   *chunk = C;
 }
 
-// Sparse geometry: waves per unit (one workgroup per unit).
-int srswa_waves(const uocr_route* r, int32_t req) {
-  int W = req > 0 ? req : kSparseWaves;
-  const int tasks = r->topk + (1024 + uocr::kBlock - 1) / uocr::kBlock;
-  if (W > tasks) W = tasks;
-  if (W > 8) W = 8;
-  if (W < 1) W = 1;
-  return W;
+// Sparse decode geometry: workgroups per unit.  num_splits > 0 is taken as
+// given (at most 64); 0 gives one workgroup per unit when the units alone
+// fill the chip, otherwise enough to put about 256 workgroups in flight
+// (at most 8 per unit: a unit has at most topk live blocks and the window).
+int srswa_splits_of(const uocr_shape* sh, int32_t req) {
+  if (req > 0) return req < 64 ? req : 64;
+  const int units = units_of(sh);
+  if (units >= kCUs) return 1;
+  const int want = (kCUs + units - 1) / units;
+  return want < 8 ? want : 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -177,6 +179,22 @@ std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];
 
 int static_scratch(const char* fn, void** ptr);
+
+// page2d RoPE of a fused step: NULL (none) or positions + parameters
+int rope_args(const char* fn, const uocr_rope* r, uocr::StepArgs& a) {
+  if (!r) return UOCR_OK;
+  if (!r->page || !r->offset) return fail(UOCR_ERR_NULL, "%s: rope page / offset is NULL", fn);
+  if (!aligned4(r->page) || !aligned4(r->offset))
+    return fail(UOCR_ERR_ALIGN, "%s: rope page / offset is not 4-byte aligned", fn);
+  if (r->page_mod < 0) return fail(UOCR_ERR_SHAPE, "%s: rope page_mod %d < 0", fn, r->page_mod);
+  if (!std::isfinite(r->base) || !(r->base > 0.f))
+    return fail(UOCR_ERR_SHAPE, "%s: rope base is not a finite positive number", fn);
+  a.rope_page = r->page;
+  a.rope_offset = r->offset;
+  a.rope_page_mod = r->page_mod;
+  a.rope_base = r->base;
+  return UOCR_OK;
+}
 
 int block_index(const char* fn, const uocr_shape* shape, const uocr_route* route, const void* k_prefix,
                 const int32_t* prefix_len, const float* proj, float* kbar_idx, int32_t first_block,
@@ -534,14 +552,22 @@ int uocr_rope_page2d(const uocr_shape* shape, void* x, void* y, int32_t tokens, 
 int32_t uocr_srswa_splits(const uocr_shape* shape, const uocr_route* route, int32_t num_splits) {
   if (check_shape(shape, "uocr_srswa_splits") != UOCR_OK) return -1;
   if (check_route(shape, route, "uocr_srswa_splits") != UOCR_OK) return -1;
-  return srswa_waves(route, num_splits);
+  if (num_splits < 0) return -1;
+  return srswa_splits_of(shape, num_splits);
+}
+
+size_t uocr_srswa_workspace_bytes(const uocr_shape* shape, const uocr_route* route, int32_t num_splits) {
+  if (check_shape(shape, "uocr_srswa_workspace_bytes") != UOCR_OK) return 0;
+  if (check_route(shape, route, "uocr_srswa_workspace_bytes") != UOCR_OK) return 0;
+  if (num_splits < 0) return 0;
+  return ws_bytes_for(units_of(shape), srswa_splits_of(shape, num_splits), shape->head_dim);
 }
 
 int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route, const void* q,
                       const void* k_prefix, const void* v_prefix, const int32_t* prefix_len,
                       const int32_t* sel_idx, const float* sel_bias, const void* k_ring,
-                      const void* v_ring, const int32_t* t_gen, void* out, int32_t num_splits,
-                      void* stream) {
+                      const void* v_ring, const int32_t* t_gen, void* out, void* workspace,
+                      size_t ws_bytes, int32_t num_splits, void* stream) {
   const char* fn = "uocr_srswa_decode";
   CHECK(check_shape(shape, fn));
   CHECK(check_route(shape, route, fn));
@@ -567,6 +593,15 @@ int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route, const vo
   ALIGN4(t_gen, "t_gen");
   if (sel_bias) ALIGN4(sel_bias, "sel_bias");
   if (num_splits < 0) return fail(UOCR_ERR_SHAPE, "%s: num_splits %d < 0", fn, num_splits);
+  const int units = units_of(shape);
+  const int S = srswa_splits_of(shape, num_splits);
+  const size_t need = ws_bytes_for(units, S, shape->head_dim);
+  if (need > 0) {
+    NEED(workspace, "workspace");
+    ALIGN16(workspace, "workspace");
+    if (ws_bytes < need)
+      return fail(UOCR_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+  }
   uocr::DecodeArgs a{};
   a.q = q;
   a.k_prefix = k_prefix;
@@ -576,12 +611,16 @@ int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route, const vo
   a.v_ring = v_ring;
   a.t_gen = t_gen;
   a.out = out;
-  a.units = units_of(shape);
+  if (need > 0) {
+    a.part_ml = static_cast<float*>(workspace);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)units * S * 2 * 4));
+  }
+  a.units = units;
   a.heads = shape->heads;
   a.prefix_cap = shape->prefix_cap;
   a.window = shape->window;
-  a.splits = 1;
-  a.waves = srswa_waves(route, num_splits);
+  a.splits = S;
+  a.waves = kSparseWaves;
   a.qscale = shape->scale * 1.4426950408889634f;
   a.sel_idx = sel_idx;
   a.sel_bias = sel_bias;
@@ -593,7 +632,7 @@ int uocr_srswa_decode(const uocr_shape* shape, const uocr_route* route, const vo
 int uocr_rswa_step(const uocr_shape* shape, const void* q, const void* k_new, const void* v_new,
                    const void* k_prefix, const void* v_prefix, const int32_t* prefix_len, void* k_ring,
                    void* v_ring, const int32_t* t_gen_in, int32_t* t_gen_out, void* out, void* workspace,
-                   size_t ws_bytes, int32_t num_splits, void* stream) {
+                   size_t ws_bytes, int32_t num_splits, const uocr_rope* rope, void* stream) {
   const char* fn = "uocr_rswa_step";
   CHECK(check_shape(shape, fn));
   NEED(q, "q");
@@ -659,6 +698,7 @@ int uocr_rswa_step(const uocr_shape* shape, const void* q, const void* k_new, co
   a.v_ring = v_ring;
   a.t_gen_in = t_gen_in;
   a.t_gen_out = t_gen_out;
+  CHECK(rope_args(fn, rope, a));
   return hip_status(uocr::launch_rswa_step(shape->dtype, shape->head_dim, a, static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -667,7 +707,7 @@ int uocr_srswa_step(const uocr_shape* shape, const uocr_route* route, const void
                     const void* v_new, const void* k_prefix, const void* v_prefix, const int32_t* prefix_len,
                     const float* proj, const float* kbar_idx, void* k_ring, void* v_ring,
                     const int32_t* t_gen_in, int32_t* t_gen_out, int32_t* sel_idx, float* sel_prob,
-                    float* sel_bias, void* out, int32_t num_splits, void* stream) {
+                    float* sel_bias, void* out, int32_t num_splits, const uocr_rope* rope, void* stream) {
   const char* fn = "uocr_srswa_step";
   CHECK(check_shape(shape, fn));
   CHECK(check_route(shape, route, fn));
@@ -736,6 +776,7 @@ int uocr_srswa_step(const uocr_shape* shape, const uocr_route* route, const void
   a.sel_idx = sel_idx;
   a.sel_prob = sel_prob;
   a.sel_bias = sel_bias;
+  CHECK(rope_args(fn, rope, a));
   return hip_status(uocr::launch_srswa_step(shape->dtype, shape->head_dim, a, static_cast<hipStream_t>(stream)),
                     fn);
 }

@@ -26,10 +26,10 @@ struct DecodeArgs {
   const void* v_ring;
   const int32_t* t_gen;
   void* out;
-  float* part_ml;      // dense with splits > 1: [units][splits][2] (max, sum)
-  float* part_o;       // dense with splits > 1: [units][splits][D]
+  float* part_ml;      // splits > 1: [units][splits][2] (max, sum)
+  float* part_o;       // splits > 1: [units][splits][D]
   int units, heads, prefix_cap, window;
-  int splits;          // dense: workgroups per unit (1 for sparse)
+  int splits;          // workgroups per unit (partials merged by k_split_merge when > 1)
   int chunk;           // dense: keys per split
   int waves;           // waves per workgroup
   float qscale;        // scale * log2(e)
@@ -119,6 +119,12 @@ struct StepArgs {
   int32_t* sel_idx;
   float* sel_prob;
   float* sel_bias;
+  // page2d rotation of q and k_new before use (rope_page == null: none):
+  // the new token of sequence b sits at (rope_page[b], rope_offset[b])
+  const int32_t* rope_page;
+  const int32_t* rope_offset;
+  int rope_page_mod;
+  float rope_base;
 };
 
 constexpr int kBlock = 32;     // tokens per routing block

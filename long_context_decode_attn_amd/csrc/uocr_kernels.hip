@@ -591,8 +591,12 @@ __global__ __launch_bounds__(256) void k_split_merge(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// uocr_srswa_decode: one workgroup per unit; tasks = live selected blocks +
-// 32-row window chunks, dealt round-robin to the W waves.
+// uocr_srswa_decode: `splits` workgroups per unit.  With one, the waves are
+// shared between the window and the live selected blocks in proportion to
+// their rows; with several, the window's 32-row chunks and the live blocks
+// form one task list, cut finer when there are fewer tasks than waves in
+// all, and task i goes to wave i mod (splits x W) of the unit; each
+// workgroup leaves its partial state for k_split_merge.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(512, 4) void k_srswa_decode(DecodeArgs a) {
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(512, 4) void k_srswa_decode(DecodeArgs a) {
   __shared__ float lds_ml[kMaxWaves][2];
   __shared__ __attribute__((aligned(16))) float lds_o[kMaxWaves * D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
-  const int unit = blockIdx.x;
+  const int unit = blockIdx.x / a.splits, split = blockIdx.x - unit * a.splits;
   const int b = unit / a.heads;
   const int m = min(max(a.prefix_len[b], 0), a.prefix_cap);
   const int w = min(max(a.t_gen[b], 0), a.window);
@@ -625,47 +629,68 @@ __global__ __launch_bounds__(512, 4) void k_srswa_decode(DecodeArgs a) {
   State<G::E> st;
   st.init();
   const size_t cb = (size_t)c * 16;
-  // The waves are shared between the window and the live blocks in
-  // proportion to their rows, so that (up to 4 live blocks with 8 waves)
-  // every wave has all of its rows in flight at once: one HBM round trip.
-  const int R = w + kBlock * n_live;
-  int ww = R > 0 ? (W * w + R - 1) / R : 0;  // waves on the window
-  if (w > 0) ww = max(1, min(ww, n_live > 0 ? W - 1 : W));
-  const int wl = max(W - ww, 1);             // waves on the live blocks (wave 0 too when W = 1)
-  const int l0 = W - wl;                     // first of them
-  if (wave < ww) {
-    const int WR = (w + ww - 1) / ww;
-    const int r0 = wave * WR, nr = min(WR, w - r0);
-    if (nr > 0) {
-      const size_t base = ((size_t)unit * a.window + r0) * G::ROWB + cb;
-      attend_fit<DT, D>(static_cast<const char*>(a.k_ring) + base, static_cast<const char*>(a.v_ring) + base,
-                        nr, 0.f, q, st, grp);
+  // rows [r0, r0 + nr) of live entry tk (counted among the live entries)
+  auto live_rows = [&](int tk, int r0, int nr) {
+    uint64_t mm = mask;
+    for (int i = 0; i < tk; ++i) mm &= mm - 1;  // drop the tk lowest live entries
+    const int slot = __ffsll((unsigned long long)mm) - 1;
+    const int j = __shfl(idx, slot);
+    const float bj = __shfl(bias, slot);
+    const int row0 = j * kBlock + r0;
+    const int n = min(nr, m - row0);
+    if (n <= 0) return;
+    const size_t base = ((size_t)unit * a.prefix_cap + row0) * G::ROWB + cb;
+    attend_fit<DT, D>(static_cast<const char*>(a.k_prefix) + base, static_cast<const char*>(a.v_prefix) + base, n,
+                      bj * kLog2e, q, st, grp);
+  };
+  auto window_rows = [&](int r0, int nr) {
+    const int n = min(nr, w - r0);
+    if (n <= 0) return;
+    const size_t base = ((size_t)unit * a.window + r0) * G::ROWB + cb;
+    attend_fit<DT, D>(static_cast<const char*>(a.k_ring) + base, static_cast<const char*>(a.v_ring) + base, n, 0.f,
+                      q, st, grp);
+  };
+  if (a.splits == 1) {
+    // The waves are shared between the window and the live blocks in
+    // proportion to their rows, so that (up to 4 live blocks with 8 waves)
+    // every wave has all of its rows in flight at once: one HBM round trip.
+    const int R = w + kBlock * n_live;
+    int ww = R > 0 ? (W * w + R - 1) / R : 0;  // waves on the window
+    if (w > 0) ww = max(1, min(ww, n_live > 0 ? W - 1 : W));
+    const int wl = max(W - ww, 1);             // waves on the live blocks (wave 0 too when W = 1)
+    const int l0 = W - wl;                     // first of them
+    if (wave < ww) {
+      const int WR = (w + ww - 1) / ww;
+      window_rows(wave * WR, WR);
     }
-  }
-  if (wave >= l0 && n_live > 0) {
-    // each live block cut into cpb chunks of 32 / cpb rows
-    int cpb = 1;
-    while (2 * cpb * n_live <= wl && 2 * cpb * G::RPL <= kBlock) cpb *= 2;
-    const int rpc = kBlock / cpb;
-    for (int task = wave - l0; task < n_live * cpb; task += wl) {
-      const int tk = task / cpb, sub = task - tk * cpb;
-      uint64_t mm = mask;
-      for (int i = 0; i < tk; ++i) mm &= mm - 1;  // drop the tk lowest live entries
-      const int slot = __ffsll((unsigned long long)mm) - 1;
-      const int j = __shfl(idx, slot);
-      const float bj = __shfl(bias, slot);
-      const int r0 = j * kBlock + sub * rpc;
-      const int nr = min(rpc, m - r0);
-      if (nr <= 0) continue;
-      const size_t base = ((size_t)unit * a.prefix_cap + r0) * G::ROWB + cb;
-      attend_fit<DT, D>(static_cast<const char*>(a.k_prefix) + base, static_cast<const char*>(a.v_prefix) + base,
-                        nr, bj * kLog2e, q, st, grp);
+    if (wave >= l0 && n_live > 0) {
+      // each live block cut into cpb chunks of 32 / cpb rows
+      int cpb = 1;
+      while (2 * cpb * n_live <= wl && 2 * cpb * G::RPL <= kBlock) cpb *= 2;
+      const int rpc = kBlock / cpb;
+      for (int task = wave - l0; task < n_live * cpb; task += wl) {
+        const int tk = task / cpb, sub = task - tk * cpb;
+        live_rows(tk, sub * rpc, rpc);
+      }
+    }
+  } else {
+    // one task list over the unit's workgroups: the window's 32-row chunks,
+    // then the live blocks, each cut into cpt pieces of 32 / cpt rows
+    const int V = a.splits * W, g = split * W + wave;
+    const int wc = (w + kBlock - 1) / kBlock;
+    int cpt = 1;
+    while (2 * cpt * (wc + n_live) <= V && 2 * cpt * G::RPL <= kBlock) cpt *= 2;
+    const int rpt = kBlock / cpt;
+    for (int task = g; task < (wc + n_live) * cpt; task += V) {
+      const int tk = task / cpt, sub = task - tk * cpt;
+      if (tk < wc) window_rows(tk * kBlock + sub * rpt, rpt);
+      else live_rows(tk - wc, sub * rpt, rpt);
     }
   }
   if (W == 8)
-    wg_finish<DT, D, 8>(st, lds_ml, lds_o, a, unit, 0);
+    wg_finish<DT, D, 8>(st, lds_ml, lds_o, a, unit, split);
   else
-    wg_finish<DT, D>(st, lds_ml, lds_o, a, unit, 0);
+    wg_finish<DT, D>(st, lds_ml, lds_o, a, unit, split);
 }
 
 // ---------------------------------------------------------------------------
@@ -1970,6 +1995,86 @@ __global__ __launch_bounds__(kNgramThreads) void k_ngram_ban(NgramArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// page2d rotary embedding of one row, shared by uocr_rope_page2d and the
+// fused steps (so that both turn a row into the same bits).  Pair j < D/2 is
+// the dims (j, j + D/2); pairs j < D/4 turn by offset * theta_j, the others
+// by (page mod page_mod) * theta_(j - D/4) (the page itself when page_mod is
+// 0), theta_i = base^(-2 i / (D/2)); negative positions count as 0.  The
+// angle is formed in fp64 and brought into [-pi, pi] by Cody-Waite reduction
+// with 2 pi split in two doubles (exact to ~1e-10 rad for positions below
+// 2^24); cos and sin are then taken in fp32, and the pair is turned in fp32.
+// ---------------------------------------------------------------------------
+constexpr double kTwoPiHi = 6.283185307179586;        // 2 pi rounded to a double
+constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
+constexpr double kInvTwoPi = 0.15915494309189535;     // 1 / (2 pi) rounded
+
+__device__ __forceinline__ double rope_theta(float base, int j, int H2) {
+  const int Q4 = H2 / 2;
+  return pow((double)base, -2.0 * (double)(j < Q4 ? j : j - Q4) / (double)H2);
+}
+__device__ __forceinline__ int rope_pos(int j, int H2, int page, int offset, int page_mod) {
+  page = max(page, 0);
+  offset = max(offset, 0);
+  return j < H2 / 2 ? offset : (page_mod > 0 ? page % page_mod : page);
+}
+// (cos, sin) of pos * theta
+__device__ __forceinline__ float2 rope_cs(int pos, double theta) {
+  const double phi = (double)pos * theta;
+  const double q = rint(phi * kInvTwoPi);
+  const double r = fma(-q, kTwoPiLo, fma(-q, kTwoPiHi, phi));
+  float sn, cn;
+  sincosf((float)r, &sn, &cn);
+  return make_float2(cn, sn);
+}
+// (x0, x1) turned by the angle whose (cos, sin) is w
+__device__ __forceinline__ void rope_turn(float& x0, float& x1, float2 w) {
+  const float s0 = x0, s1 = x1;
+  x0 = fmaf(s0, w.x, -s1 * w.y);
+  x1 = fmaf(s0, w.y, s1 * w.x);
+}
+// a value rounded to the storage type and widened again
+template <int DT>
+__device__ __forceinline__ float to_storage(float x) {
+  if constexpr (DT == 0) return x;
+  else return __uint_as_float(bf16_bits(x) << 16);
+}
+// element i of a row in the storage type
+template <int DT>
+__device__ __forceinline__ float row_elem(const void* row, int i) {
+  if constexpr (DT == 0) return reinterpret_cast<const float*>(row)[i];
+  else return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16);
+}
+template <int DT>
+__device__ __forceinline__ void set_row_elem(void* row, int i, float x) {
+  if constexpr (DT == 0) reinterpret_cast<float*>(row)[i] = x;
+  else reinterpret_cast<uint16_t*>(row)[i] = (uint16_t)bf16_bits(x);
+}
+// The fused steps' rotation of one decode step (a.rope_page set): thread
+// j < D/2 turns pair j of the unit's q into s_q (rounded to the storage
+// type, as a separate uocr_rope_page2d call stores it) and, when kring is
+// not null, pair j of k_new into the ring row kring.
+template <int DT, int D>
+__device__ __forceinline__ void step_rope(const StepArgs& a, int unit, int b, float* s_q, void* kring) {
+  constexpr int H2 = D / 2;
+  const int j = threadIdx.x;
+  if (j >= H2) return;
+  const float2 w = rope_cs(rope_pos(j, H2, a.rope_page[b], a.rope_offset[b], a.rope_page_mod),
+                           rope_theta(a.rope_base, j, H2));
+  const char* qrow = static_cast<const char*>(a.d.q) + (size_t)unit * D * (DT == 0 ? 4 : 2);
+  float q0 = row_elem<DT>(qrow, j), q1 = row_elem<DT>(qrow, j + H2);
+  rope_turn(q0, q1, w);
+  s_q[j] = to_storage<DT>(q0);
+  s_q[j + H2] = to_storage<DT>(q1);
+  if (kring) {
+    const char* krow = static_cast<const char*>(a.k_new) + (size_t)unit * D * (DT == 0 ? 4 : 2);
+    float k0 = row_elem<DT>(krow, j), k1 = row_elem<DT>(krow, j + H2);
+    rope_turn(k0, k1, w);
+    set_row_elem<DT>(kring, j, k0);
+    set_row_elem<DT>(kring, j + H2, k1);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fused steps: append + (route +) decode in one launch
 // ---------------------------------------------------------------------------
 // uocr_srswa_step: one workgroup of NT threads per unit runs the whole step.
@@ -2001,9 +2106,11 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   __shared__ float l_bias[kMaxTopk];
   __shared__ float lds_ml[W][2];
   __shared__ __attribute__((aligned(16))) float lds_o[W * D];
+  __shared__ __attribute__((aligned(16))) float s_q[D];  // the rotated q (page2d RoPE only)
   const DecodeArgs& d = a.d;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x, b = unit / d.heads, h = unit - b * d.heads;
+  const bool rope = a.rope_page != nullptr;
   const int grp = lane / G::LPR, c = lane % G::LPR;
   const size_t cb = (size_t)c * 16;
 
@@ -2061,6 +2168,15 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   const int n = d.window, slot = t % n, w = min(n, t + 1);
   const int nb = (m + kBlock - 1) / kBlock;
 
+  // page2d RoPE: q is turned into s_q and the turned k_new row written into
+  // its ring slot (pair-wise), before anything reads them; the block keys'
+  // loads are already in flight
+  if (rope) {
+    step_rope<DT, D>(a, unit, b, s_q, static_cast<char*>(a.k_ring) + ((size_t)unit * n + slot) * G::ROWB);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < DPS; ++k) qv_[k] = s_q[sl_q * DPS + k];
+  }
   {
     double acc = 0.0;
 #pragma unroll
@@ -2068,15 +2184,21 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
     s_red[sl_q][i_q] = acc;
   }
 
-  // ring append of this unit's row, and the new count
-  if (tid < 2 * CPR)
+  // ring append of this unit's row (with RoPE the k row is already in), and
+  // the new count
+  if (tid < 2 * CPR && (a_which || !rope))
     *reinterpret_cast<uint4*>(static_cast<char*>(a_which ? a.v_ring : a.k_ring) +
                               ((size_t)unit * n + slot) * G::ROWB + a_off * 16) = new_chunk;
   if (h == 0 && tid == 0) a.t_gen_out[b] = t + 1;
   if (tid == 0) tsm.flag = 0;  // zeroed before the first workgroup barrier
 
   float q[G::E];
-  load_q<DT, D>(d.q, unit, c, d.qscale, q);
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) q[e] = s_q[c * G::E + e] * d.qscale;
+  } else {
+    load_q<DT, D>(d.q, unit, c, d.qscale, q);
+  }
   State<G::E> st;
   st.init();
   __syncthreads();
@@ -2117,7 +2239,7 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   // Window attention on waves 1 .. W-1 while wave 0 routes: every slot of
   // the ring is addressable, so each of these waves reads its share of all n
   // slots and lets only the first w count; the new token's row is taken from
-  // k_new / v_new.
+  // k_new / v_new (with RoPE, from its ring slot, written before a barrier).
   auto window = [&]() {
     const int WR = (n + W - 2) / (W - 1);
     const int r0 = (wave - 1) * WR, r1 = min(r0 + WR, n);
@@ -2127,7 +2249,7 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
       constexpr int UW = (20 + G::RPL - 1) / G::RPL < 8 ? (20 + G::RPL - 1) / G::RPL : 8;
       attend_range<DT, D, UW, STREAM>(static_cast<const char*>(d.k_ring) + base,
                                       static_cast<const char*>(d.v_ring) + base, r1 - r0, 0.f, q, st, grp,
-                                      slot - r0, static_cast<const char*>(a.k_new) + nbase,
+                                      rope ? -1 : slot - r0, static_cast<const char*>(a.k_new) + nbase,
                                       static_cast<const char*>(a.v_new) + nbase, w - r0);
     }
   };
@@ -2180,11 +2302,16 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
 // uocr_rswa_step: the dense decode with the append fused in.  Every
 // workgroup reads the new token's row from k_new / v_new instead of the ring
 // slot it goes to; the workgroup of split 0 writes it into the ring.
+// With page2d RoPE every workgroup turns q itself (into LDS), and the
+// workgroup whose keys hold the new token's position writes the turned k row
+// (and the v row) into the ring and reads them back from there after a
+// barrier.
 template <int DT, int D>
 __global__ __launch_bounds__(1024) void k_rswa_step(StepArgs a) {
   using G = Geo<DT, D>;
   __shared__ float lds_ml[kMaxWaves][2];
   __shared__ __attribute__((aligned(16))) float lds_o[kMaxWaves * D];
+  __shared__ __attribute__((aligned(16))) float s_q[D];
   const DecodeArgs& d = a.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int unit = blockIdx.x / d.splits, split = blockIdx.x - unit * d.splits;
@@ -2192,21 +2319,37 @@ __global__ __launch_bounds__(1024) void k_rswa_step(StepArgs a) {
   const int m = min(max(d.prefix_len[b], 0), d.prefix_cap);
   const int t = max(a.t_gen_in[b], 0);
   const int n = d.window, slot = t % n, w = min(n, t + 1);
+  const bool rope = a.rope_page != nullptr;
+  const int lo = split * d.chunk, hi = min(lo + d.chunk, m + w);
   constexpr int CPR = G::ROWB / 16;
-  if (split == 0 && threadIdx.x < 2 * CPR) {
+  char* const kslot = static_cast<char*>(a.k_ring) + ((size_t)unit * n + slot) * G::ROWB;
+  char* const vslot = static_cast<char*>(a.v_ring) + ((size_t)unit * n + slot) * G::ROWB;
+  if (rope) {
+    const bool owner = m + slot >= lo && m + slot < hi;  // exactly one workgroup of the unit
+    step_rope<DT, D>(a, unit, b, s_q, owner ? kslot : nullptr);
+    if (owner && threadIdx.x >= D / 2 && threadIdx.x < D / 2 + CPR) {
+      const int off = threadIdx.x - D / 2;
+      *reinterpret_cast<uint4*>(vslot + off * 16) =
+          ld16(static_cast<const char*>(a.v_new) + (size_t)unit * G::ROWB + off * 16);
+    }
+    __syncthreads();
+  } else if (split == 0 && threadIdx.x < 2 * CPR) {
     const int which = threadIdx.x / CPR, off = threadIdx.x - which * CPR;
     const char* src = static_cast<const char*>(which ? a.v_new : a.k_new) + (size_t)unit * G::ROWB + off * 16;
-    char* dst = static_cast<char*>(which ? a.v_ring : a.k_ring) + ((size_t)unit * n + slot) * G::ROWB + off * 16;
-    *reinterpret_cast<uint4*>(dst) = ld16(src);
+    *reinterpret_cast<uint4*>((which ? vslot : kslot) + off * 16) = ld16(src);
   }
   if (split == 0 && h == 0 && threadIdx.x == 0) a.t_gen_out[b] = t + 1;
 
-  const int lo = split * d.chunk, hi = min(lo + d.chunk, m + w);
   const int per = hi > lo ? (hi - lo + W - 1) / W : 0;
   const int wlo = lo + wave * per, whi = min(wlo + per, hi);
   const int grp = lane / G::LPR, c = lane % G::LPR;
   float q[G::E];
-  load_q<DT, D>(d.q, unit, c, d.qscale, q);
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) q[e] = s_q[c * G::E + e] * d.qscale;
+  } else {
+    load_q<DT, D>(d.q, unit, c, d.qscale, q);
+  }
   State<G::E> st;
   st.init();
   const size_t cb = (size_t)c * 16;
@@ -2220,7 +2363,7 @@ __global__ __launch_bounds__(1024) void k_rswa_step(StepArgs a) {
     const size_t base = ((size_t)unit * n + w0) * G::ROWB + cb;
     const size_t nb_ = (size_t)unit * G::ROWB + cb;
     attend_range<DT, D>(static_cast<const char*>(d.k_ring) + base, static_cast<const char*>(d.v_ring) + base,
-                        w1 - w0, 0.f, q, st, grp, slot - w0, static_cast<const char*>(a.k_new) + nb_,
+                        w1 - w0, 0.f, q, st, grp, rope ? -1 : slot - w0, static_cast<const char*>(a.k_new) + nb_,
                         static_cast<const char*>(a.v_new) + nb_);
   }
   if (W == 4)
@@ -2246,9 +2389,6 @@ __global__ __launch_bounds__(1024) void k_rswa_step(StepArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kRopeThreads = 256;
 constexpr int kRopeInFlight = 8;                       // chunk pairs per thread in flight
-constexpr double kTwoPiHi = 6.283185307179586;        // 2 pi rounded to a double
-constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
-constexpr double kInvTwoPi = 0.15915494309189535;     // 1 / (2 pi) rounded
 
 __device__ __forceinline__ void st16_stream(char* p, const uint4& v) {
   __builtin_nontemporal_store(v4u32{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u32*>(p));
@@ -2257,7 +2397,7 @@ __device__ __forceinline__ void st16_stream(char* p, const uint4& v) {
 template <int DT, int D>
 __global__ __launch_bounds__(kRopeThreads) void k_rope_page2d(RopeArgs a) {
   using G = Geo<DT, D>;
-  constexpr int H2 = D / 2, Q4 = D / 4;
+  constexpr int H2 = D / 2;
   constexpr int CPH = H2 / G::E;                        // 16-byte chunks per half row
   constexpr int AE = kRopeTokens * H2 / kRopeThreads;   // (token, pair) entries per thread
   static_assert(kRopeThreads % H2 == 0 && AE >= 1, "every entry of a thread has the same pair");
@@ -2290,8 +2430,7 @@ __global__ __launch_bounds__(kRopeThreads) void k_rope_page2d(RopeArgs a) {
     pos[k] = 0;
     if (ti < nt) {
       const size_t pi = (size_t)b * a.tokens + t0 + ti;
-      const int pg = max(a.page[pi], 0), off = max(a.offset[pi], 0);
-      pos[k] = j < Q4 ? off : (a.page_mod > 0 ? pg % a.page_mod : pg);
+      pos[k] = rope_pos(j, H2, a.page[pi], a.offset[pi], a.page_mod);
     }
   }
   uint4 u0[kRopeInFlight], u1[kRopeInFlight];
@@ -2304,16 +2443,11 @@ __global__ __launch_bounds__(kRopeThreads) void k_rope_page2d(RopeArgs a) {
       u1[k] = ld16_stream(p + G::ROWB / 2);
     }
   }
-  const double theta = pow((double)a.base, -2.0 * (double)(j < Q4 ? j : j - Q4) / (double)H2);
+  const double theta = rope_theta(a.base, j, H2);
 #pragma unroll
   for (int k = 0; k < AE; ++k) {
     const int ti = tid / H2 + k * (kRopeThreads / H2);
-    const double phi = (double)pos[k] * theta;
-    const double q = rint(phi * kInvTwoPi);
-    const double r = fma(-q, kTwoPiLo, fma(-q, kTwoPiHi, phi));
-    float sn, cn;
-    sincosf((float)r, &sn, &cn);
-    cs[ti][j] = make_float2(cn, sn);
+    cs[ti][j] = rope_cs(pos[k], theta);
   }
   __syncthreads();
   auto turn = [&](const uint4& v0, const uint4& v1, long long e) {
@@ -2325,12 +2459,7 @@ __global__ __launch_bounds__(kRopeThreads) void k_rope_page2d(RopeArgs a) {
     unpack(v0, x0);
     unpack(v1, x1);
 #pragma unroll
-    for (int i = 0; i < G::E; ++i) {
-      const float2 w = cs[ti][c * G::E + i];
-      const float s0 = x0[i], s1 = x1[i];
-      x0[i] = fmaf(s0, w.x, -s1 * w.y);
-      x1[i] = fmaf(s0, w.y, s1 * w.x);
-    }
+    for (int i = 0; i < G::E; ++i) rope_turn(x0[i], x1[i], cs[ti][c * G::E + i]);
     if constexpr (DT == 0) {
       st16_stream(p, make_uint4(__float_as_uint(x0[0]), __float_as_uint(x0[1]), __float_as_uint(x0[2]),
                                 __float_as_uint(x0[3])));
@@ -2400,7 +2529,10 @@ hipError_t launch_rswa_decode(int dtype, int head_dim, const DecodeArgs& a, hipS
 }
 
 hipError_t launch_srswa_decode(int dtype, int head_dim, const DecodeArgs& a, hipStream_t s) {
-  UOCR_DISPATCH(k_srswa_decode, dim3((unsigned)a.units), dim3(64 * a.waves), a);
+  UOCR_DISPATCH(k_srswa_decode, dim3((unsigned)((long)a.units * a.splits)), dim3(64 * a.waves), a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  UOCR_DISPATCH(k_split_merge, dim3((unsigned)((a.units + 3) / 4)), dim3(256), a);
   return hipGetLastError();
 }
 

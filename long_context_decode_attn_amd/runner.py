@@ -39,9 +39,17 @@ def layers_for(step_bytes: int, minimum: int = 12) -> int:
 
 class LayeredDecoder:
     def __init__(self, w: S.Workload, layers: int, num_splits: int = 0, fused: bool = True,
-                 base: Optional[DecodeSession] = None, device: str = "cuda"):
+                 base: Optional[DecodeSession] = None, device: str = "cuda", rope: bool = False):
         self.w = w
         self.fused = fused
+        # page2d RoPE fused into the steps: each sequence's new token at
+        # (page, offset) positions of a seeded multi-page document
+        self.rope = None
+        if rope:
+            assert fused, "RoPE is fused into the step kernels only"
+            page, offset = S.page_positions(3, w.batch, 1, first_page=w.pages - 1, start_offset=17)
+            self.rope = (torch.from_numpy(np.ascontiguousarray(page[:, 0])).to(device),
+                         torch.from_numpy(np.ascontiguousarray(offset[:, 0])).to(device), 2, 10000.0)
         if base is None:
             base = DecodeSession(w, device=device, num_splits=num_splits, fused=fused)
         self.layers: List[DecodeSession] = [base] + [base.clone() for _ in range(layers - 1)]
@@ -72,7 +80,7 @@ class LayeredDecoder:
         s = self.layers[layer]
         if self.fused:
             sel = (self.sel_idx[g], self.sel_prob[g], self.sel_bias[g]) if self.w.sparse else None
-            s.fused_step(self.q[g], self.k[g], self.v[g], out=self.out[g], sel=sel)
+            s.fused_step(self.q[g], self.k[g], self.v[g], out=self.out[g], sel=sel, rope=self.rope)
         else:   # one launch per row; outputs stay in the session's own buffers
             s.step(self.q[g], self.k[g], self.v[g])
 

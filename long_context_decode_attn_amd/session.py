@@ -65,7 +65,8 @@ class DecodeSession:
             self.sel_idx = torch.empty((B, H, k), dtype=torch.int32, device=device)
             self.sel_prob = torch.empty((B, H, k), dtype=torch.float32, device=device)
             self.sel_bias = torch.empty((B, H, k), dtype=torch.float32, device=device)
-            self.workspace = None
+            self.workspace = U.alloc_workspace(U.uocr_srswa_workspace_bytes(self.shape, self.route, num_splits),
+                                               device)
         else:
             self.workspace = U.alloc_workspace(U.uocr_rswa_workspace_bytes(self.shape, num_splits), device)
 
@@ -109,25 +110,27 @@ class DecodeSession:
         if self.w.sparse:
             U.uocr_srswa_decode(self.shape, self.route, q, self.k_prefix, self.v_prefix, self.prefix_len,
                                 self.sel_idx, self.sel_bias, self.k_ring, self.v_ring, self.t_gen, self.out,
-                                self.num_splits)
+                                self.workspace, self.num_splits)
         else:
             U.uocr_rswa_decode(self.shape, q, self.k_prefix, self.v_prefix, self.prefix_len, self.k_ring,
                                self.v_ring, self.t_gen, self.out, self.workspace, self.num_splits)
 
-    def fused_step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out=None, sel=None) -> None:
+    def fused_step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, out=None, sel=None,
+                   rope=None) -> None:
         """The whole step in one launch; the generated-token counts move to
         the other buffer, which becomes `t_gen`.  out (and, for SR-SWA, sel =
-        (idx, prob, bias)) default to the session's own buffers."""
+        (idx, prob, bias)) default to the session's own buffers; rope = None
+        or (page, offset, page_mod, base) turns q and k_new by page2d RoPE."""
         out = self.out if out is None else out
         if self.w.sparse:
             si, sp, sb = (self.sel_idx, self.sel_prob, self.sel_bias) if sel is None else sel
             U.uocr_srswa_step(self.shape, self.route, q, k_new, v_new, self.k_prefix, self.v_prefix,
                               self.prefix_len, self.proj, self.kbar, self.k_ring, self.v_ring, self.t_gen,
-                              self.t_gen_next, si, sp, sb, out, self.num_splits)
+                              self.t_gen_next, si, sp, sb, out, self.num_splits, rope=rope)
         else:
             U.uocr_rswa_step(self.shape, q, k_new, v_new, self.k_prefix, self.v_prefix, self.prefix_len,
                              self.k_ring, self.v_ring, self.t_gen, self.t_gen_next, out, self.workspace,
-                             self.num_splits)
+                             self.num_splits, rope=rope)
         self.t_gen, self.t_gen_next = self.t_gen_next, self.t_gen
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor) -> torch.Tensor:

@@ -46,6 +46,11 @@ class _Route(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("idx_dim", ctypes.c_int32), ("topk", ctypes.c_int32)]
 
 
+class _Rope(ctypes.Structure):
+    _fields_ = [("page", ctypes.c_void_p), ("offset", ctypes.c_void_p), ("page_mod", ctypes.c_int32),
+                ("base", ctypes.c_float)]
+
+
 @dataclasses.dataclass(frozen=True)
 class Shape:
     batch: int
@@ -122,10 +127,11 @@ def load_library():
                                           _P]),
         "uocr_rope_page2d": (ctypes.c_int, [SP, _P, _P, _I32, _P, _P, _I32, ctypes.c_float, _P]),
         "uocr_srswa_splits": (_I32, [SP, RP, _I32]),
-        "uocr_srswa_decode": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
-        "uocr_rswa_step": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P]),
+        "uocr_srswa_workspace_bytes": (_SZ, [SP, RP, _I32]),
+        "uocr_srswa_decode": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P]),
+        "uocr_rswa_step": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I32, _P, _P]),
         "uocr_srswa_step": (ctypes.c_int, [SP, RP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                           _P, _I32, _P]),
+                                           _P, _I32, _P, _P]),
         "uocr_calib_read": (ctypes.c_int, [_P, _SZ, _I32, _P, _P]),
         "uocr_calib_empty": (ctypes.c_int, [_I32, _I32, _P]),
         "uocr_calib_pull": (ctypes.c_int, [_P, _SZ, _I32, _I32, _I32, _P, _P]),
@@ -144,7 +150,7 @@ def load_library():
 EXPORTED = ("uocr_ring_append", "uocr_rswa_splits", "uocr_rswa_workspace_bytes",
             "uocr_rswa_decode", "uocr_rswa_decode_static", "uocr_block_index_build", "uocr_block_index_range", "uocr_block_score", "uocr_entmax15_topk",
             "uocr_prefill_route", "uocr_ngram_ban", "uocr_rope_page2d",
-            "uocr_srswa_splits", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
+            "uocr_srswa_splits", "uocr_srswa_workspace_bytes", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
             "uocr_status_string", "uocr_last_error", "uocr_version",
             "uocr_calib_read", "uocr_calib_empty", "uocr_calib_pull")
 
@@ -347,8 +353,13 @@ def uocr_rope_page2d(shape: Shape, x, page, offset, page_mod: int = 2, base: flo
           base, _stream(stream))
 
 
+def uocr_srswa_workspace_bytes(shape: Shape, route: Route, num_splits: int = 0) -> int:
+    return int(load_library().uocr_srswa_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(route.c()),
+                                                         num_splits))
+
+
 def uocr_srswa_decode(shape: Shape, route: Route, q, k_prefix, v_prefix, prefix_len, sel_idx, sel_bias,
-                      k_ring, v_ring, t_gen, out, num_splits: int = 0, stream=None) -> None:
+                      k_ring, v_ring, t_gen, out, workspace=None, num_splits: int = 0, stream=None) -> None:
     B, H, D, n, m, dt = shape.batch, shape.heads, shape.head_dim, shape.window, shape.prefix_cap, shape.torch_dtype
     _check(q, "q", dt, (B, H, D))
     _check(k_prefix, "k_prefix", dt, (B, H, m, D))
@@ -362,11 +373,22 @@ def uocr_srswa_decode(shape: Shape, route: Route, q, k_prefix, v_prefix, prefix_
     _check(out, "out", dt, (B, H, D))
     _call("uocr_srswa_decode", ctypes.byref(shape.c()), ctypes.byref(route.c()), _ptr(q), _ptr(k_prefix),
           _ptr(v_prefix), _ptr(prefix_len), _ptr(sel_idx), _ptr(sel_bias), _ptr(k_ring), _ptr(v_ring),
-          _ptr(t_gen), _ptr(out), num_splits, _stream(stream))
+          _ptr(t_gen), _ptr(out), *_ws(workspace), num_splits, _stream(stream))
+
+
+def _rope(rope, batch: int):
+    """rope = None or (page, offset, page_mod, base) with page, offset [B] int32
+    device tensors: the position of each sequence's new token."""
+    if rope is None:
+        return None
+    page, offset, page_mod, base = rope
+    _check(page, "rope page", torch.int32, (batch,))
+    _check(offset, "rope offset", torch.int32, (batch,))
+    return ctypes.byref(_Rope(page.data_ptr(), offset.data_ptr(), page_mod, base))
 
 
 def uocr_rswa_step(shape: Shape, q, k_new, v_new, k_prefix, v_prefix, prefix_len, k_ring, v_ring, t_gen_in,
-                   t_gen_out, out, workspace=None, num_splits: int = 0, stream=None) -> None:
+                   t_gen_out, out, workspace=None, num_splits: int = 0, rope=None, stream=None) -> None:
     B, H, D, n, m, dt = shape.batch, shape.heads, shape.head_dim, shape.window, shape.prefix_cap, shape.torch_dtype
     for t, name, shp in [(q, "q", (B, H, D)), (k_new, "k_new", (B, H, D)), (v_new, "v_new", (B, H, D)),
                          (k_prefix, "k_prefix", (B, H, m, D)), (v_prefix, "v_prefix", (B, H, m, D)),
@@ -378,12 +400,12 @@ def uocr_rswa_step(shape: Shape, q, k_new, v_new, k_prefix, v_prefix, prefix_len
     wp, wb = _ws(workspace)
     _call("uocr_rswa_step", ctypes.byref(shape.c()), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_prefix),
           _ptr(v_prefix), _ptr(prefix_len), _ptr(k_ring), _ptr(v_ring), _ptr(t_gen_in), _ptr(t_gen_out), _ptr(out),
-          wp, wb, num_splits, _stream(stream))
+          wp, wb, num_splits, _rope(rope, B), _stream(stream))
 
 
 def uocr_srswa_step(shape: Shape, route: Route, q, k_new, v_new, k_prefix, v_prefix, prefix_len, proj, kbar_idx,
                     k_ring, v_ring, t_gen_in, t_gen_out, sel_idx, sel_prob, sel_bias, out, num_splits: int = 0,
-                    stream=None) -> None:
+                    rope=None, stream=None) -> None:
     B, H, D, n, m, dt, k = (shape.batch, shape.heads, shape.head_dim, shape.window, shape.prefix_cap,
                             shape.torch_dtype, route.topk)
     for t, name, shp in [(q, "q", (B, H, D)), (k_new, "k_new", (B, H, D)), (v_new, "v_new", (B, H, D)),
@@ -401,7 +423,7 @@ def uocr_srswa_step(shape: Shape, route: Route, q, k_new, v_new, k_prefix, v_pre
     _call("uocr_srswa_step", ctypes.byref(shape.c()), ctypes.byref(route.c()), _ptr(q), _ptr(k_new), _ptr(v_new),
           _ptr(k_prefix), _ptr(v_prefix), _ptr(prefix_len), _ptr(proj), _ptr(kbar_idx), _ptr(k_ring), _ptr(v_ring),
           _ptr(t_gen_in), _ptr(t_gen_out), _ptr(sel_idx), _ptr(sel_prob), _ptr(sel_bias), _ptr(out), num_splits,
-          _stream(stream))
+          _rope(rope, B), _stream(stream))
 
 
 # ----------------------------------------------------------------------------

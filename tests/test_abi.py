@@ -97,12 +97,20 @@ def test_route_validation():
     big = _shape(U, prefix_cap=4097 * 32)
     r = U._Route(32, 32, 16)
     assert lib.uocr_entmax15_topk(ctypes.byref(big), ctypes.byref(r), FAKE, FAKE, FAKE, None, FAKE, None) == -6
-    assert lib.uocr_srswa_decode(ctypes.byref(sh), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
-                                 FAKE, 1, None) == -1
-    assert lib.uocr_srswa_decode(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
-                                 FAKE, FAKE, 1, None) == -1
-    assert lib.uocr_srswa_decode(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
-                                 FAKE, FAKE, -1, None) == -2
+    def srswa(route, sel=FAKE, ws=None, wsb=0, splits=1):
+        return lib.uocr_srswa_decode(ctypes.byref(sh), route, FAKE, FAKE, FAKE, FAKE, sel, None, FAKE, FAKE, FAKE,
+                                     FAKE, ws, wsb, splits, None)
+    assert srswa(None) == -1
+    assert srswa(ctypes.byref(r), sel=None) == -1
+    assert srswa(ctypes.byref(r), splits=-1) == -2
+    # several workgroups per unit need the workspace uocr_srswa_workspace_bytes gives
+    need = lib.uocr_srswa_workspace_bytes(ctypes.byref(sh), ctypes.byref(r), 4)
+    assert need == U.uocr_srswa_workspace_bytes(U.Shape(2, 3, 128, 320), U.Route(), 4) > 0
+    assert lib.uocr_srswa_workspace_bytes(ctypes.byref(sh), ctypes.byref(r), 1) == 0
+    assert lib.uocr_srswa_splits(ctypes.byref(sh), ctypes.byref(r), 0) == 8      # 6 units: about 256 workgroups
+    assert srswa(ctypes.byref(r), splits=4) == -1
+    assert srswa(ctypes.byref(r), ws=FAKE, wsb=need - 1, splits=4) == -4
+    assert srswa(ctypes.byref(r), ws=ODD, wsb=need, splits=4) == -5
     assert lib.uocr_ring_append(ctypes.byref(sh), FAKE, FAKE, FAKE, ODD, FAKE, None) == -5
     assert lib.uocr_block_index_build(ctypes.byref(sh), ctypes.byref(r), FAKE, FAKE, None, FAKE, None) == -1
 
@@ -191,11 +199,14 @@ def test_split_geometry():
         S = U.uocr_rswa_splits(sh)
         assert 1 <= S <= max(1, -(-(m + 128) // 32))
         assert U.uocr_rswa_splits(sh, 10 ** 6) <= -(-(m + 128) // 16)
+    # sparse decode: workgroups per unit, enough for ~256 workgroups when the
+    # units alone do not fill the chip
     r = U.Route()
-    sh = U.Shape(8, 10, 128, 32000)
-    assert U.uocr_srswa_splits(sh, r) == 8            # waves per unit
-    assert U.uocr_srswa_splits(sh, r, 1) == 1
-    assert U.uocr_srswa_splits(sh, r, 99) == 8
+    assert U.uocr_srswa_splits(U.Shape(8, 10, 128, 32000), r) == 4       # 80 units -> 320 workgroups
+    assert U.uocr_srswa_splits(U.Shape(32, 10, 128, 10240), r) == 1      # 320 units
+    assert U.uocr_srswa_splits(U.Shape(1, 2, 128, 528), r) == 8          # at most 8 per unit
+    assert U.uocr_srswa_splits(U.Shape(8, 10, 128, 32000), r, 1) == 1
+    assert U.uocr_srswa_splits(U.Shape(8, 10, 128, 32000), r, 99) == 64
 
 
 def test_product_path_has_no_oracle_or_fallback():

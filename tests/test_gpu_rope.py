@@ -136,3 +136,81 @@ def test_rope_prefill_chunk_shape_sampled():
     sample += [(0, 0), (B - 1, T - 1)]
     got, want = _run(B, 10, T, 128, "bf16", page_tokens=400, first_page=2, start_offset=100, sample=sample)
     _check(got, want, "bf16", "prefill chunk")
+
+
+# ----------------------------------------------------------------------------
+# page2d RoPE fused into the decode steps
+# ----------------------------------------------------------------------------
+def _stored(t, dtype):
+    """Device tensor -> storage bits (bf16 as uint16, f32 as uint32)."""
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("sparse,dtype,D,num_splits", [(True, "bf16", 128, 0), (True, "f32", 64, 0),
+                                                        (True, "bf16", 64, 4), (False, "bf16", 128, 0),
+                                                        (False, "bf16", 128, 3), (False, "f32", 128, 8)])
+def test_fused_step_with_rope(sparse, dtype, D, num_splits):
+    """uocr_srswa_step / uocr_rswa_step with page2d RoPE equal, bit for bit,
+    uocr_rope_page2d on (q, k_new) followed by the step without it (output,
+    selection, rings, counts), over several steps with per-sequence counts
+    before and across a wrap; and the output agrees with the oracle run on
+    the oracle's own rotation (queries and the ring's keys turned in fp64)."""
+    from long_context_decode_attn_amd.session import DecodeSession
+    from tests._gpu_common import HostMirror
+    need_gpu()
+    w = S.Workload("rope-step", batch=3, heads=2, head_dim=D, dtype=dtype, pages=5, prompt=7, t0=0, steps=4,
+                   seed=77, sparse=sparse, planted=6 if sparse else 0, fixed_query=sparse, topk=4)
+    say("fused rope", sparse, dtype, D, num_splits)
+    t0 = [0, 50, 126]
+    ring = S.initial_ring(w, t0)
+    kv = S.prefix_kv(w)
+    fused = DecodeSession(w, prefix_kv=kv, ring=ring, fused=True, num_splits=num_splits)
+    plain = DecodeSession(w, prefix_kv=kv, ring=ring, fused=True, num_splits=num_splits)
+    host = HostMirror(w, prefix_kv=kv, ring=ring)
+    if sparse:
+        fused.build_index()
+        plain.build_index()
+    page, offset = S.page_positions(9, w.batch, w.steps, page_tokens=300, first_page=2, start_offset=40)
+    page_mod, base = 2, 10000.0
+    P = S.projection(w).astype(np.float64) if sparse else None
+    for step in range(w.steps):
+        q, k, v = S.step_inputs(w, step)
+        tq, tk, tv = to_device(q, dtype), to_device(k, dtype), to_device(v, dtype)
+        pg = torch.from_numpy(np.ascontiguousarray(page[:, step])).cuda()
+        of = torch.from_numpy(np.ascontiguousarray(offset[:, step])).cuda()
+        fused.fused_step(tq, tk, tv, rope=(pg, of, page_mod, base))
+        # the separate path: rotate copies of q and k_new, then the plain step
+        q2, k2 = tq.clone(), tk.clone()
+        U.uocr_rope_page2d(plain.shape, q2.view(w.batch, w.heads, 1, D), pg.view(w.batch, 1), of.view(w.batch, 1),
+                           page_mod, base, y=k2.view(w.batch, w.heads, 1, D))
+        plain.fused_step(q2, k2, tv)
+        torch.cuda.synchronize()
+        assert torch.equal(tq, to_device(q, dtype)) and torch.equal(tk, to_device(k, dtype)), "inputs modified"
+        assert torch.equal(fused.out, plain.out), f"step {step}: output differs from rope + step"
+        assert torch.equal(fused.t_gen, plain.t_gen)
+        assert np.array_equal(_stored(fused.k_ring, dtype), _stored(plain.k_ring, dtype)), f"step {step}: k ring"
+        assert np.array_equal(_stored(fused.v_ring, dtype), _stored(plain.v_ring, dtype)), f"step {step}: v ring"
+        if sparse:
+            assert torch.equal(fused.sel_idx, plain.sel_idx) and torch.equal(fused.sel_bias, plain.sel_bias)
+            assert torch.equal(fused.sel_prob, plain.sel_prob)
+        # oracle: q and k_new turned in fp64; the ring keeps the turned keys
+        qd, kd = S.widen(q, dtype), S.widen(k, dtype)
+        for b in range(w.batch):
+            qd[b] = O.rope_page2d(qd[b], int(page[b, step]), int(offset[b, step]), page_mod, base)
+            kd[b] = O.rope_page2d(kd[b], int(page[b, step]), int(offset[b, step]), page_mod, base)
+        O.ring_append(host.Kr, host.Vr, host.t_gen, kd, S.widen(v, dtype))
+        ref = np.zeros((w.batch, w.heads, D))
+        for b in range(w.batch):
+            for h in range(w.heads):
+                wk, wv = host.window(b, h)
+                if sparse:
+                    kb = O.block_index(host.Kp[b, h], w.prefix_len, P)
+                    idx, _, bias = O.route_unit(O.as_f32(O.block_scores(qd[b, h], P, kb)), w.topk)
+                    assert np.array_equal(fused.sel_idx[b, h].cpu().numpy(), idx), (step, b, h)
+                    ref[b, h] = O.srswa_unit(qd[b, h], host.Kp[b, h], host.Vp[b, h], w.prefix_len, idx, bias, wk, wv,
+                                             w.scale)
+                else:
+                    ref[b, h] = O.rswa_unit(qd[b, h], host.Kp[b, h], host.Vp[b, h], w.prefix_len, wk, wv, w.scale)
+        assert_close(to_host(fused.out), ref, dtype, f"fused rope step {step}")

@@ -194,17 +194,20 @@ def test_entmax_topk_one_wave_ties_and_signed_zeros(nb):
                                     what=f"nb={nb} b={b} h={h}")
 
 
-@pytest.mark.parametrize("live,with_bias", [(0, True), (1, True), (5, True), (16, True), (16, False)])
-def test_srswa_decode_given_selection(live, with_bias):
+@pytest.mark.parametrize("live,with_bias,num_splits", [(0, True, 0), (1, True, 0), (5, True, 0), (16, True, 0),
+                                                        (16, False, 0), (16, True, 1), (5, True, 3), (16, True, 64)])
+def test_srswa_decode_given_selection(live, with_bias, num_splits):
     """Sparse decode on its own, for a given routing result: every live
-    block, dead blocks (bias -inf, never read: their rows are NaN), -1 padding."""
+    block, dead blocks (bias -inf, never read: their rows are NaN), -1 padding;
+    one workgroup per unit or several (merged through the workspace; 64 leaves
+    most workgroups without rows)."""
     need_gpu()
     w = _small_sparse(batch=3, heads=2, pages=3, prompt=20, t0=0)
-    say("srswa given selection", live, with_bias)
+    say("srswa given selection", live, with_bias, num_splits)
     t0 = [0, 7, 300]
     Kr, Vr, tg = S.initial_ring(w, t0)
     kv = S.prefix_kv(w)
-    sess = DecodeSession(w, prefix_kv=kv, ring=(Kr, Vr, tg))
+    sess = DecodeSession(w, prefix_kv=kv, ring=(Kr, Vr, tg), num_splits=num_splits)
     host = HostMirror(w, prefix_kv=kv, ring=(Kr, Vr, tg))
     nb = w.n_blocks
     idx, bias = S.random_selection(5 + live, w.units, nb, 16, live)
@@ -228,7 +231,8 @@ def test_srswa_decode_given_selection(live, with_bias):
     sess.sel_idx.copy_(torch.from_numpy(idx))
     sb = None if bias is None else torch.from_numpy(bias).cuda()
     U.uocr_srswa_decode(sess.shape, sess.route, to_device(q, "bf16"), sess.k_prefix, sess.v_prefix,
-                        sess.prefix_len, sess.sel_idx, sb, sess.k_ring, sess.v_ring, sess.t_gen, sess.out)
+                        sess.prefix_len, sess.sel_idx, sb, sess.k_ring, sess.v_ring, sess.t_gen, sess.out,
+                        sess.workspace, num_splits)
     torch.cuda.synchronize()
     qd = S.widen(q, "bf16")
     got = to_host(sess.out)
@@ -405,7 +409,7 @@ def test_srswa_reduces_to_dense_when_every_block_is_kept():
     q, _, _ = S.step_inputs(w, 0)
     qt = to_device(q, "bf16")
     U.uocr_srswa_decode(sess.shape, sess.route, qt, sess.k_prefix, sess.v_prefix, sess.prefix_len, sess.sel_idx,
-                        None, sess.k_ring, sess.v_ring, sess.t_gen, sess.out)
+                        None, sess.k_ring, sess.v_ring, sess.t_gen, sess.out, sess.workspace)
     dense.attend(qt)
     torch.cuda.synchronize()
     qd = S.widen(q, "bf16")
