@@ -307,8 +307,9 @@ int uocr_rope_page2d(const uocr_shape* shape, void* x, void* y, int32_t tokens,
  *   sel_bias NULL means bias 0 for every selected block.  A block whose bias
  *   is -inf has weight exactly 0 and is not read at all.
  *   A unit's live blocks and window rows are shared among num_splits
- *   workgroups (0 = one per unit when there are at least 256 units, else
- *   enough for about 256 workgroups, at most 8 per unit; uocr_srswa_splits
+ *   workgroups (0 = one per unit when there are at least as many units as
+ *   the device has compute units (256 on MI355X), else about one workgroup
+ *   per compute unit in all, at most 8 per unit; uocr_srswa_splits
  *   gives the count); with more than one, each leaves its (max, sum, partial
  *   output) in the workspace and a second kernel in the same stream merges
  *   them, as in uocr_rswa_decode.  Size the workspace with

@@ -116,7 +116,30 @@ size_t ws_bytes_for(int units, int splits, int head_dim) {
 
 constexpr int kDenseWaves = 4;    // waves per workgroup of the dense decode
 constexpr int kSparseWaves = 8;   // waves per workgroup of the sparse decode and step (default)
-constexpr int kCUs = 256;         // compute units of an MI355X
+constexpr int kDefaultCUs = 256;  // compute units of an MI355X, when no device answers
+constexpr int kMaxCuDevices = 64;
+std::mutex g_cu_mu;
+int g_cus[kMaxCuDevices];
+
+// Compute units of the current device (asked once per device); 256 when no
+// device can be asked (e.g. argument queries on a host without a GPU).
+int device_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxCuDevices) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  std::lock_guard<std::mutex> lock(g_cu_mu);
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = kDefaultCUs;
+    }
+    g_cus[dev] = n;
+  }
+  return g_cus[dev];
+}
 constexpr int kMaxPrefillQueries = 1 << 20;  // queries per unit in one prefill routing call
 
 // Dense split geometry: workgroups per unit and keys per workgroup for the
@@ -130,16 +153,17 @@ void rswa_geometry(const uocr_shape* sh, int32_t req, int* splits, int* chunk) {
     S = req;
   } else {
     // The fewest splits (longest chunks, least merging) whose workgroups
-    // fill the 256 CUs of the chip and spread evenly over them: at least 256
-    // workgroups, and the busiest CU holds no more than 1/0.93 of the mean
+    // fill the device's CUs (256 on MI355X) and spread evenly over them: at
+    // least one per CU, and the busiest CU holds no more than 1/0.93 of the mean
     // (measured: 480 workgroups stream at 80% of peak, 560 at 69%).  Chunks
     // stay >= 512 keys; failing that, aim at ~2048 workgroups.
     const int cap = (L + 511) / 512;
+    const int cus = device_cus();
     S = 0;
     for (int s = 1; s <= cap && S == 0; ++s) {
       const long long n = (long long)units * s;
-      const long long slots = (n + kCUs - 1) / kCUs * kCUs;
-      if (n >= kCUs && n * 100 >= slots * 93) S = s;
+      const long long slots = (n + cus - 1) / cus * cus;
+      if (n >= cus && n * 100 >= slots * 93) S = s;
     }
     if (S == 0) {
       const int want = (2048 + units - 1) / units;
@@ -156,14 +180,15 @@ void rswa_geometry(const uocr_shape* sh, int32_t req, int* splits, int* chunk) {
 }
 
 // Sparse decode geometry: workgroups per unit.  num_splits > 0 is taken as
-// given (at most 64); 0 gives one workgroup per unit when the units alone
-// fill the chip, otherwise enough to put about 256 workgroups in flight
-// (at most 8 per unit: a unit has at most topk live blocks and the window).
+// given (at most 64); 0 gives one workgroup per unit when there are as many
+// units as compute units, otherwise about one workgroup per compute unit in
+// all (at most 8 per unit: a unit has at most topk live blocks and the window).
 int srswa_splits_of(const uocr_shape* sh, int32_t req) {
   if (req > 0) return req < 64 ? req : 64;
   const int units = units_of(sh);
-  if (units >= kCUs) return 1;
-  const int want = (kCUs + units - 1) / units;
+  const int cus = device_cus();
+  if (units >= cus) return 1;
+  const int want = (cus + units - 1) / units;
   return want < 8 ? want : 8;
 }
 
