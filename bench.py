@@ -39,13 +39,15 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("5bfe89ffc2decf68", 45166878, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("5bfe89ffc2decf68", 18900476, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("5bfe89ffc2decf68", 892188055, 1024675),
-    ("uocr_rswa_step", "dense-1p-b512"): ("5bfe89ffc2decf68", 1092835108, 3940452),
-    ("uocr_rswa_step", "dense-40p-b32"): ("5bfe89ffc2decf68", 1699294832, 686865),
-    ("uocr_rswa_step", "dense-125p-b8"): ("5bfe89ffc2decf68", 1316291734, 302168),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("5bfe89ffc2decf68", 169078300, 167787446),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("ba318f8c79c6b8fb", 45216351, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("ba318f8c79c6b8fb", 18932434, 76928),
+    ("uocr_srswa_step", "srswa-40p-b32-wide"): ("ba318f8c79c6b8fb", 118652346, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8-wide"): ("ba318f8c79c6b8fb", 37088166, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("ba318f8c79c6b8fb", 892105958, 1024645),
+    ("uocr_rswa_step", "dense-1p-b512"): ("ba318f8c79c6b8fb", 1092735337, 3940431),
+    ("uocr_rswa_step", "dense-40p-b32"): ("ba318f8c79c6b8fb", 1699098542, 686852),
+    ("uocr_rswa_step", "dense-125p-b8"): ("ba318f8c79c6b8fb", 1316160607, 302161),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("ba318f8c79c6b8fb", 169090983, 167803957),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
@@ -542,9 +544,11 @@ def _graph_time_us(fn, per_graph=32, reps=20):
 
 def calibrate_main(args):
     """Denominators measured on this machine: a plain and a nontemporal read
-    stream over 2 GiB, an empty launch at the decode steps' grids, and the
-    time workgroups take to pull their own bytes when only some compute
-    units are busy (uocr_calib_* in include/uocr_calib.h)."""
+    stream over 2 GiB, an empty launch at the decode steps' grids, the time
+    workgroups take to pull their own bytes when only some compute units are
+    busy, when the workgroups of a launch start on each XCD, and what merging
+    workgroups' partials inside one kernel costs (uocr_calib_* in
+    include/uocr_calib.h)."""
     import torch
 
     from long_context_decode_attn_amd import uocr as U
@@ -584,6 +588,35 @@ def calibrate_main(args):
                                          "per_group_gbs": round(per / (us * 1e-6) / 1e9, 2)}
         print(json.dumps({"step": "pull", "groups": groups}), flush=True)
     out["pull_512_threads_nontemporal"] = pull
+    # start of the workgroups of one launch, by XCD (workgroup g runs on XCD
+    # g mod 8): the real-time counter runs at 100 MHz
+    starts = {}
+    for groups in (80, 320):
+        st = torch.zeros(groups, dtype=torch.int64, device="cuda")
+        _graph_time_us(lambda: U.uocr_calib_start(groups, 512, st), per_graph=8, reps=4)
+        t = st.cpu().numpy().astype(np.int64)
+        t0 = int(t.min())
+        starts[f"{groups}x512"] = {f"xcd{x}": round(float((t[x::8] - t0).min()) / 100.0, 3) for x in range(8)}
+        starts[f"{groups}x512"]["last_start_us"] = round(float(t.max() - t0) / 100.0, 3)
+    out["workgroup_start_us_by_xcd"] = starts
+    print(json.dumps({"step": "starts", **starts}), flush=True)
+    # merging workgroups' partials inside one kernel (no workgroup waits; the
+    # last to arrive merges) against an empty launch of the same grid
+    ex = {}
+    for units, split in ((80, 4), (320, 2), (320, 4)):
+        part = torch.zeros(units * split * 130, dtype=torch.float32, device="cuda")
+        cnt = torch.zeros(units, dtype=torch.int32, device="cuda")
+        res = torch.zeros(units * 130, dtype=torch.float32, device="cuda")
+        row = {"empty": round(_graph_time_us(lambda: U.uocr_calib_empty(units * split, 256)), 3)}
+        for mode, name in ((2, "count_only"), (1, "agent_atomics"), (0, "threadfence")):
+            res.zero_()
+            row[name] = round(_graph_time_us(lambda: U.uocr_calib_exchange(mode, units, split, part, cnt, res),
+                                             per_graph=16, reps=5), 3)
+            if mode != 2:
+                want = split * (split + 1) / 2 + split * torch.arange(130, device="cuda", dtype=torch.float32)
+                row[name + "_merged_right"] = bool(torch.equal(res.view(units, 130), want.expand(units, 130)))
+        ex[f"{units}x{split}"] = row
+    out["merge_inside_one_kernel_us"] = ex
     print(json.dumps(out), flush=True)
 
 

@@ -12,7 +12,10 @@
  *   - uocr_calib_pull: each of `groups` workgroups reads its own contiguous
  *     run of bytes_per_group bytes and nothing else, the time one compute
  *     unit needs to bring in a given amount of data when only some units of
- *     the chip are busy (the floor of a step whose units each read that much).
+ *     the chip are busy (the floor of a step whose units each read that much);
+ *   - uocr_calib_start: when each workgroup of a launch starts;
+ *   - uocr_calib_exchange: what merging several workgroups' partial states
+ *     inside one kernel costs (instead of a second kernel).
  *
  * Conventions as in uocr.h: device pointers, the caller owns every buffer,
  * stream is a hipStream_t passed as void* (NULL = default stream), the call
@@ -48,6 +51,25 @@ int uocr_calib_empty(int32_t groups, int32_t threads, void* stream);
  * groups * bytes_per_group bytes.  sink: `groups` uint32.                   */
 int uocr_calib_pull(const void* src, size_t bytes_per_group, int32_t groups, int32_t threads,
                     int32_t nontemporal, uint32_t* sink, void* stream);
+
+/* Thread 0 of every workgroup of a grid of `groups` x `threads` stores the
+ * device's constant-rate real-time counter (100 MHz on MI355X) as the
+ * workgroup starts: stamps[g] for workgroup g (`groups` uint64).  Workgroups
+ * are dealt to the XCDs in turn (g mod 8), so the stamps show how the start
+ * of a launch spreads over the chip.                                        */
+int uocr_calib_start(int32_t groups, int32_t threads, uint64_t* stamps, void* stream);
+
+/* The cost of merging partial states inside one kernel: `units` x `split`
+ * workgroups of 256 threads; each writes a partial of 130 floats to
+ * part[(unit * split + s) * 130 ...] and adds one to count[unit]; the
+ * workgroup that arrives last (no workgroup ever waits) sums its unit's
+ * partials into out[unit * 130 ...] and sets count[unit] back to 0.
+ * mode 0: plain stores and loads around __threadfence(); mode 1: agent-scope
+ * relaxed atomic stores and loads of the partials; mode 2: the count alone.
+ * count must start at 0 (it is left at 0); part holds units * split * 130
+ * floats, out units * 130.  1 <= units * split <= 2^20.                     */
+int uocr_calib_exchange(int32_t mode, int32_t units, int32_t split, float* part, int32_t* count, float* out,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
 // Measurement kernels (include/uocr_calib.h): a streaming read of a large
-// buffer, an empty launch and a per-workgroup pull.  They give the decode
+// buffer, an empty launch, a per-workgroup pull, the start times of a grid's
+// workgroups and the cost of merging workgroups' partials inside one kernel.  They give the decode
 // kernels' denominators on the machine at hand; none of them is part of the
 // method.
 #include "../../include/uocr_calib.h"
@@ -69,6 +70,56 @@ __global__ __launch_bounds__(1024) void k_calib_pull(const v4u32* __restrict__ s
   if (h == kNever) sink[blockIdx.x] = h;
 }
 
+// Start time of every workgroup (the constant-rate real-time counter, read
+// by thread 0 as the workgroup begins), for the spread of start times across
+// the chip.
+__global__ void k_calib_start(uint64_t* stamps) {
+  if (threadIdx.x == 0) stamps[blockIdx.x] = wall_clock64();
+}
+
+// Merging the partial states of `split` workgroups per unit inside one
+// kernel: every workgroup writes a partial of kPart floats and adds one to
+// its unit's counter; the workgroup that arrives last sums the unit's
+// partials, writes out[unit] and clears the counter.  Nothing waits: the
+// last to arrive does the merge.  MODE 0: plain stores and loads with a
+// device-wide fence (__threadfence) before the count and after it; MODE 1:
+// agent-scope relaxed atomic stores and loads of the partials, the count
+// after a workgroup-scope fence (which waits for the stores); MODE 2: the
+// count alone.
+constexpr int kPart = 130;
+template <int MODE>
+__global__ __launch_bounds__(256) void k_calib_exchange(float* part, int32_t* count, float* out, int split) {
+  const int unit = blockIdx.x / split, s = blockIdx.x - unit * split;
+  __shared__ int last;
+  float* mine = part + ((size_t)unit * split + s) * kPart;
+  if constexpr (MODE != 2) {
+    for (int t = threadIdx.x; t < kPart; t += blockDim.x) {
+      const float v = (float)(s + 1) + (float)t;
+      if constexpr (MODE == 1) __hip_atomic_store(mine + t, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else mine[t] = v;
+    }
+  }
+  if constexpr (MODE == 0) __threadfence();
+  else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(count + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == split - 1;
+  __syncthreads();
+  if (!last) return;
+  if constexpr (MODE == 0) __threadfence();
+  for (int t = threadIdx.x; t < kPart; t += blockDim.x) {
+    float acc = 0.f;
+    for (int k = 0; k < split; ++k) {
+      const float* src = part + ((size_t)unit * split + k) * kPart + t;
+      if constexpr (MODE == 1) acc += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if constexpr (MODE == 0) acc += *src;
+      else acc += 1.f;
+    }
+    out[(size_t)unit * kPart + t] = acc;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(count + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 bool threads_ok(int32_t t) { return t == 64 || t == 128 || t == 256 || t == 512 || t == 1024; }
 
 }  // namespace
@@ -108,6 +159,25 @@ int uocr_calib_pull(const void* src, size_t bytes_per_group, int32_t groups, int
     k_calib_pull<true><<<groups, threads, 0, s>>>(p, bytes_per_group / 16, sink);
   else
     k_calib_pull<false><<<groups, threads, 0, s>>>(p, bytes_per_group / 16, sink);
+  return hipGetLastError() == hipSuccess ? UOCR_OK : UOCR_ERR_HIP;
+}
+
+int uocr_calib_start(int32_t groups, int32_t threads, uint64_t* stamps, void* stream) {
+  if (!stamps) return UOCR_ERR_NULL;
+  if (groups < 1 || groups > (1 << 20) || !threads_ok(threads)) return UOCR_ERR_SHAPE;
+  k_calib_start<<<groups, threads, 0, static_cast<hipStream_t>(stream)>>>(stamps);
+  return hipGetLastError() == hipSuccess ? UOCR_OK : UOCR_ERR_HIP;
+}
+
+int uocr_calib_exchange(int32_t mode, int32_t units, int32_t split, float* part, int32_t* count, float* out,
+                        void* stream) {
+  if (!part || !count || !out) return UOCR_ERR_NULL;
+  if (mode < 0 || mode > 2 || units < 1 || split < 1 || (int64_t)units * split > (1 << 20)) return UOCR_ERR_SHAPE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 g((unsigned)(units * split)), b(256);
+  if (mode == 0) k_calib_exchange<0><<<g, b, 0, s>>>(part, count, out, split);
+  else if (mode == 1) k_calib_exchange<1><<<g, b, 0, s>>>(part, count, out, split);
+  else k_calib_exchange<2><<<g, b, 0, s>>>(part, count, out, split);
   return hipGetLastError() == hipSuccess ? UOCR_OK : UOCR_ERR_HIP;
 }
 

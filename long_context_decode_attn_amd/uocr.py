@@ -135,6 +135,8 @@ def load_library():
         "uocr_calib_read": (ctypes.c_int, [_P, _SZ, _I32, _P, _P]),
         "uocr_calib_empty": (ctypes.c_int, [_I32, _I32, _P]),
         "uocr_calib_pull": (ctypes.c_int, [_P, _SZ, _I32, _I32, _I32, _P, _P]),
+        "uocr_calib_start": (ctypes.c_int, [_I32, _I32, _P, _P]),
+        "uocr_calib_exchange": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, _P, _P]),
         "uocr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "uocr_last_error": (ctypes.c_char_p, []),
         "uocr_version": (ctypes.c_int, []),
@@ -152,7 +154,7 @@ EXPORTED = ("uocr_ring_append", "uocr_rswa_splits", "uocr_rswa_workspace_bytes",
             "uocr_prefill_route", "uocr_ngram_ban", "uocr_rope_page2d",
             "uocr_srswa_splits", "uocr_srswa_workspace_bytes", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
             "uocr_status_string", "uocr_last_error", "uocr_version",
-            "uocr_calib_read", "uocr_calib_empty", "uocr_calib_pull")
+            "uocr_calib_read", "uocr_calib_empty", "uocr_calib_pull", "uocr_calib_start", "uocr_calib_exchange")
 
 
 # ----------------------------------------------------------------------------
@@ -453,6 +455,19 @@ def uocr_calib_pull(src: torch.Tensor, bytes_per_group: int, groups: int, thread
     _check(sink, "sink", torch.int32, (groups,))
     _calib_call("uocr_calib_pull", _ptr(src), bytes_per_group, groups, threads, int(nontemporal), _ptr(sink),
                 _stream(stream))
+
+
+def uocr_calib_start(groups: int, threads: int, stamps: torch.Tensor, stream=None) -> None:
+    _check(stamps, "stamps", torch.int64, (groups,))
+    _calib_call("uocr_calib_start", groups, threads, _ptr(stamps), _stream(stream))
+
+
+def uocr_calib_exchange(mode: int, units: int, split: int, part: torch.Tensor, count: torch.Tensor,
+                        out: torch.Tensor, stream=None) -> None:
+    _check(part, "part", torch.float32, (units * split * 130,))
+    _check(count, "count", torch.int32, (units,))
+    _check(out, "out", torch.float32, (units * 130,))
+    _calib_call("uocr_calib_exchange", mode, units, split, _ptr(part), _ptr(count), _ptr(out), _stream(stream))
 
 
 def uocr_version() -> int:
