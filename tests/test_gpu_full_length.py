@@ -55,12 +55,12 @@ def _windows(w, L, layer, T):
     return np.stack(ks, axis=2), np.stack(vs, axis=2)
 
 
-def _run(name, steps=None):
+def _run(name, steps=None, layers=LAYERS):
     need_gpu()
     w = S.WORKLOADS[name]
     steps = w.steps if steps is None else steps
     assert steps % 2 == 0
-    L = LAYERS
+    L = layers
     say(f"full-length {name}: {L} layers x {steps} steps, graphs of {2 * L} steps")
     dec = LayeredDecoder(w, L, fused=True)
     dec.build_index()
@@ -154,3 +154,10 @@ def _run(name, steps=None):
 def test_full_length_timed_configuration(name):
     flags, swaps = _run(name)
     assert swaps <= flags
+
+
+def test_full_length_high_concurrency_dense():
+    """512 sequences x 10 heads (one page + prompt) for 1000 steps on 4
+    layers (the same graphs, fewer layers, so that drawing the per-step
+    inputs of 512 sequences stays within a minute)."""
+    _run("dense-1p-b512", layers=4)
