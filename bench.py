@@ -39,15 +39,15 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("ba318f8c79c6b8fb", 45216351, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("ba318f8c79c6b8fb", 18932434, 76928),
-    ("uocr_srswa_step", "srswa-40p-b32-wide"): ("ba318f8c79c6b8fb", 118652346, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8-wide"): ("ba318f8c79c6b8fb", 37088166, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("ba318f8c79c6b8fb", 892105958, 1024645),
-    ("uocr_rswa_step", "dense-1p-b512"): ("ba318f8c79c6b8fb", 1092735337, 3940431),
-    ("uocr_rswa_step", "dense-40p-b32"): ("ba318f8c79c6b8fb", 1699098542, 686852),
-    ("uocr_rswa_step", "dense-125p-b8"): ("ba318f8c79c6b8fb", 1316160607, 302161),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("ba318f8c79c6b8fb", 169090983, 167803957),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("79ab4e0c72fb3432", 45186684, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("79ab4e0c72fb3432", 18909846, 76928),
+    ("uocr_srswa_step", "srswa-40p-b32-wide"): ("79ab4e0c72fb3432", 118624123, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8-wide"): ("79ab4e0c72fb3432", 37066603, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("79ab4e0c72fb3432", 892113006, 1024674),
+    ("uocr_rswa_step", "dense-1p-b512"): ("79ab4e0c72fb3432", 1092754718, 3940448),
+    ("uocr_rswa_step", "dense-40p-b32"): ("79ab4e0c72fb3432", 1699107151, 686881),
+    ("uocr_rswa_step", "dense-125p-b8"): ("79ab4e0c72fb3432", 1316158628, 302180),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("79ab4e0c72fb3432", 169068478, 167790668),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--calibrate", action="store_true",
                     help="instead of the decode step, measure the denominators: plain and nontemporal read "
                          "streams over 2 GiB, empty launches and per-workgroup pulls")
+    ap.add_argument("--phases", action="store_true",
+                    help="instead of the throughput line, where the time of one fused SR-SWA step goes: the "
+                         "phase stamps of every workgroup, from libuocr_stamps.so")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (known bytes) so that a "
                          "counter profile of this run can scale FETCH_SIZE / WRITE_SIZE")
@@ -621,6 +624,116 @@ def calibrate_main(args):
 
 
 # ----------------------------------------------------------------------------
+def _quantiles(x):
+    x = np.asarray(x, dtype=np.float64).ravel()
+    return {"p10": round(float(np.percentile(x, 10)), 3), "p50": round(float(np.median(x)), 3),
+            "p90": round(float(np.percentile(x, 90)), 3), "max": round(float(x.max()), 3)}
+
+
+def phases_main(args):
+    """--phases: the phase stamps of the fused SR-SWA step (include/uocr_calib.h,
+    uocr_phase_stamps) in the bench's own setup (cloned layers, a HIP graph of
+    two steps per layer), read after each of `reps` replays: they are those
+    of the graph's last launch, which follows the others back to back.  Times
+    are microseconds after the first workgroup of that launch started."""
+    from long_context_decode_attn_amd import synth as S
+    w = S.WORKLOADS[args.workload]
+    if not w.sparse:
+        print("--phases times the fused SR-SWA step: pick a sparse workload", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from long_context_decode_attn_amd import uocr as U
+    from long_context_decode_attn_amd.runner import LayeredDecoder
+    from long_context_decode_attn_amd.session import DecodeSession
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    U.use_phase_stamps()
+    U.load_library()
+    torch.cuda.set_device(0)
+    base = DecodeSession(w, num_splits=args.num_splits, fused=True)
+    base.build_index()
+    n_layers = args.layers if args.layers > 0 else _layers_needed(w, base)
+    dec = LayeredDecoder(w, n_layers, num_splits=args.num_splits, fused=True, base=base, rope=args.rope)
+    dec.build_index()
+    dec.fill_pool(64)
+    dec.run_eager(args.warmup)
+    graph = dec.capture()
+    graph.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(20):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    us_step = start.elapsed_time(stop) * 1e3 / (20 * dec.G)
+
+    units, W, reps = w.units, (args.num_splits or 8), 40
+    rows = []
+    for _ in range(reps):
+        graph.replay()
+        rows.append(U.uocr_phase_stamps(units).astype(np.int64))
+    A = np.stack(rows)                                   # [reps, units, 64]
+    t = (A - A[:, :, 0].min(axis=1)[:, None, None]) * 0.01   # us after the launch's first start
+    t0 = t[:, :, 0]
+    win = t[:, :, 17:16 + W].max(axis=2)                 # waves 1 .. W-1
+    live = t[:, :, 48:48 + W].max(axis=2)
+    end = t[:, :, 4]
+    span = end.max(axis=1)
+    xcc = A[0, :, 3] & 0xF
+    hw = A[0, :, 8]
+    cu = (xcc << 8) | ((hw >> 8) & 0xFF)                  # XCD, engine, array, CU
+    _, inv, cnt = np.unique(cu, return_inverse=True, return_counts=True)
+    shared = cnt[inv] > 1                                # units whose CU ran two or more of them
+    life = end - t0
+    res = {
+        "workload": w.name, "units": units, "waves": W, "layers_cycled": dec.L, "replays": reps,
+        "stamping_build_us_per_step": round(us_step, 3),
+        "launch_span_us": _quantiles(span),
+        "gap_between_launches_us": round(us_step - float(np.median(span)), 3),
+        "start_us": _quantiles(t0),
+        "q_idx_us": _quantiles(t[:, :, 5] - t0),
+        "first_keys_scored_us": _quantiles(t[:, :, 6] - t0),
+        "scores_in_lds_us": _quantiles(t[:, :, 1] - t0),
+        "routed_us": _quantiles(t[:, :, 2] - t0),
+        "window_done_us": _quantiles(win - t0),
+        "live_done_us": _quantiles(live - t0),
+        "merge_groups_done_us": _quantiles(t[:, :, 56:56 + W].max(axis=2) - t0),
+        "merge_barrier_us": _quantiles(t[:, :, 7] - t0),
+        "end_us": _quantiles(life),
+        "routing_us": _quantiles(t[:, :, 2] - t[:, :, 1]),
+        "window_after_scores_us": _quantiles(win - t[:, :, 1]),
+        "live_after_routing_us": _quantiles(live - np.maximum(t[:, :, 2], win)),
+        "finish_us": _quantiles(end - live),
+        "cus_used": int(len(cnt)), "units_on_shared_cus": int(shared.sum()),
+        "end_us_alone": _quantiles(life[:, ~shared]) if (~shared).any() else None,
+        "end_us_shared": _quantiles(life[:, shared]) if shared.any() else None,
+        "units_per_xcd": np.bincount(xcc.astype(np.int64), minlength=8).tolist(),
+        "start_us_p50_by_xcd": [round(float(np.median(t0[:, xcc == k])), 3) if (xcc == k).any() else None
+                                for k in range(8)],
+        "kernel_source": kernel_source_hash(),
+    }
+    print(json.dumps({"phases": res}), flush=True)
+
+
+def _layers_needed(w, base):
+    """Layers to cycle: enough that the steps' working set is twice the
+    Infinity Cache; the sparse step's bytes depend on the live blocks,
+    measured on one step of a scratch copy."""
+    from long_context_decode_attn_amd import synth as S
+    from long_context_decode_attn_amd.runner import layers_for
+    from long_context_decode_attn_amd.session import to_device
+    live_est = None
+    if w.sparse:
+        probe = base.clone()
+        q, k, v = S.step_inputs(w, 0)
+        probe.step(to_device(q, w.dtype), to_device(k, w.dtype), to_device(v, w.dtype))
+        live_est = int(np.sum((probe.sel_idx.cpu().numpy() >= 0) & np.isfinite(probe.sel_bias.cpu().numpy())))
+        del probe
+    return layers_for(sum(algorithmic_bytes(w, live_est).values()))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -636,6 +749,8 @@ def main():
         return rope_main(args)
     if args.ngram_ban:
         return ngram_main(args)
+    if args.phases:
+        return phases_main(args)
 
     from long_context_decode_attn_amd import synth as S
     w = S.WORKLOADS[args.workload]
@@ -647,7 +762,7 @@ def main():
     import torch
 
     from long_context_decode_attn_amd import uocr as U
-    from long_context_decode_attn_amd.runner import LayeredDecoder, layers_for
+    from long_context_decode_attn_amd.runner import LayeredDecoder
     from long_context_decode_attn_amd.session import DecodeSession
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -659,19 +774,7 @@ def main():
     if w.sparse:
         base.build_index()   # the first launch also loads the kernel; the build is timed below
 
-    # layers: enough that the steps' working set is twice the Infinity Cache;
-    # the sparse step's bytes depend on the live blocks, measured on one step
-    # of a scratch copy
-    live_est = None
-    if w.sparse:
-        probe = base.clone()
-        from long_context_decode_attn_amd.session import to_device
-        q, k, v = S.step_inputs(w, 0)
-        probe.step(to_device(q, w.dtype), to_device(k, w.dtype), to_device(v, w.dtype))
-        live_est = int(np.sum((probe.sel_idx.cpu().numpy() >= 0) & np.isfinite(probe.sel_bias.cpu().numpy())))
-        del probe
-    est_bytes = sum(algorithmic_bytes(w, live_est).values())
-    n_layers = args.layers if args.layers > 0 else layers_for(est_bytes)
+    n_layers = args.layers if args.layers > 0 else _layers_needed(w, base)
     dec = LayeredDecoder(w, n_layers, num_splits=args.num_splits, fused=fused, base=base, rope=args.rope)
     torch.cuda.synchronize()
 

@@ -15,7 +15,9 @@
  *     the chip are busy (the floor of a step whose units each read that much);
  *   - uocr_calib_start: when each workgroup of a launch starts;
  *   - uocr_calib_exchange: what merging several workgroups' partial states
- *     inside one kernel costs (instead of a second kernel).
+ *     inside one kernel costs (instead of a second kernel);
+ *   - uocr_phase_stamps: when each phase of the fused SR-SWA step ends, per
+ *     workgroup (a separately built library records them).
  *
  * Conventions as in uocr.h: device pointers, the caller owns every buffer,
  * stream is a hipStream_t passed as void* (NULL = default stream), the call
@@ -70,6 +72,33 @@ int uocr_calib_start(int32_t groups, int32_t threads, uint64_t* stamps, void* st
  * floats, out units * 130.  1 <= units * split <= 2^20.                     */
 int uocr_calib_exchange(int32_t mode, int32_t units, int32_t split, float* part, int32_t* count, float* out,
                         void* stream);
+
+/* Phase stamps of the fused SR-SWA step (uocr_srswa_step): where the time of
+ * one launch goes, workgroup by workgroup.  Only the library built with
+ * UOCR_PHASE_STAMPS (libuocr_stamps.so, the same sources) records them; in
+ * libuocr.so this call returns UOCR_ERR_UNSUPPORTED and the step kernels hold
+ * no stamping code.  Copies the stamps of units [0, units) left by the
+ * latest uocr_srswa_step launches (each launch overwrites its units' rows)
+ * into host memory dst[units][64] (uint64) after the work queued on `stream`
+ * is done, and returns when the copy is complete; 1 <= units <= 4096.
+ * Each value is the device's 100 MHz real-time counter (common to all XCDs)
+ * when the phase ended, recorded by thread 0 or by lane 0 of wave w:
+ *   0 the workgroup starts            5 q_idx = P^T q formed
+ *   6 the first batch of block keys scored   1 every block score in LDS
+ *   2 wave 0 has routed the unit and published the selection
+ *  32+w wave w (w >= 1) has the selection (all waves stamp 2 or 32+w at the
+ *     same point, after seeing it published)
+ *  16+w wave w (w >= 1) has attended over its share of the window
+ *  48+w wave w has attended over its live blocks
+ *  56+w wave w has left its share of the merge in LDS
+ *   7 the workgroup merge's barrier has passed
+ *   4 the output row is written
+ *   3 (not a time) the XCD the workgroup ran on (hardware register XCC_ID)
+ *   8 (not a time) hardware register HW_ID of wave 0: bits 8-11 the compute
+ *     unit, 12 the shader array, 13-15 the shader engine within the XCD
+ * Slots 16+w and 48+w are taken after the wave's loads have all arrived
+ * (the stamping build waits for them there).  Other slots are unspecified. */
+int uocr_phase_stamps(uint64_t* dst, int32_t units, void* stream);
 
 #ifdef __cplusplus
 }

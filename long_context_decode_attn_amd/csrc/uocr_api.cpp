@@ -1,6 +1,7 @@
 // C ABI of libuocr.so: host-side validation, launch geometry and status codes.
 // Declarations and the meaning of every argument: include/uocr.h.
 #include "../../include/uocr.h"
+#include "../../include/uocr_calib.h"
 
 #include <hip/hip_runtime.h>
 
@@ -804,6 +805,19 @@ int uocr_srswa_step(const uocr_shape* shape, const uocr_route* route, const void
   CHECK(rope_args(fn, rope, a));
   return hip_status(uocr::launch_srswa_step(shape->dtype, shape->head_dim, a, static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int uocr_phase_stamps(uint64_t* dst, int32_t units, void* stream) {
+  const char* fn = "uocr_phase_stamps";
+  if (!dst) return fail(UOCR_ERR_NULL, "%s: dst is NULL", fn);
+  if (units < 1 || units > uocr::kMaxStampUnits)
+    return fail(UOCR_ERR_SHAPE, "%s: units %d is not in [1, %d]", fn, units, uocr::kMaxStampUnits);
+  const hipError_t e = uocr::read_phase_stamps(dst, (size_t)units * 64 * sizeof(uint64_t),
+                                               static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(UOCR_ERR_UNSUPPORTED, "%s: this library records no stamps (libuocr_stamps.so does)", fn);
+  if (e != hipSuccess) return fail(UOCR_ERR_HIP, "%s: copy failed: %s", fn, hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"

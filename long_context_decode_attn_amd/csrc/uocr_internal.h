@@ -145,4 +145,11 @@ hipError_t launch_rope_page2d(int dtype, int head_dim, const RopeArgs& a, hipStr
 hipError_t launch_srswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
 hipError_t launch_rswa_step(int dtype, int head_dim, const StepArgs& a, hipStream_t s);
 
+// Phase stamps of the last fused SR-SWA steps (a library built with
+// UOCR_PHASE_STAMPS; hipErrorNotSupported otherwise): copies the first
+// `bytes` of the [kMaxStampUnits][64] uint64 stamp array to host memory and
+// waits for the copy.
+constexpr int kMaxStampUnits = 4096;
+hipError_t read_phase_stamps(void* dst, size_t bytes, hipStream_t s);
+
 }  // namespace uocr

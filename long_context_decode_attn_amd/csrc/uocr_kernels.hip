@@ -35,6 +35,34 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFloor = -1.0e30f;
 constexpr int kWaves = 4;  // waves per workgroup of the block-index kernel
 
+// Phase stamps of the fused SR-SWA step, compiled in only with
+// UOCR_PHASE_STAMPS (the library libuocr_stamps.so; libuocr.so has none of
+// this code).  One thread records the device's constant-rate real-time
+// counter (100 MHz) into LDS as a phase ends, and the workgroup copies its
+// 64 slots to g_stamps[unit] once at the very end, so that no global store
+// adds a wait to the step's barriers.  UOCR_STAMP_DONE first waits for every
+// load in flight, so that a phase counts as done when its data has arrived,
+// not when its last load was issued.  The slots are listed with
+// uocr_phase_stamps in include/uocr_calib.h.
+#ifdef UOCR_PHASE_STAMPS
+constexpr int kStampSlots = 64;
+__device__ unsigned long long g_stamps[kMaxStampUnits * kStampSlots];
+#define UOCR_STAMP_LDS __shared__ unsigned long long s_stamp[kStampSlots]
+#define UOCR_STAMP(st, cond, slot)                 \
+  do {                                             \
+    if (cond) (st)[slot] = wall_clock64();         \
+  } while (0)
+#define UOCR_STAMP_DONE(st, cond, slot)            \
+  do {                                             \
+    __builtin_amdgcn_s_waitcnt(0);                 \
+    if (cond) (st)[slot] = wall_clock64();         \
+  } while (0)
+#else
+#define UOCR_STAMP_LDS unsigned long long* const s_stamp = nullptr
+#define UOCR_STAMP(st, cond, slot) ((void)(st))
+#define UOCR_STAMP_DONE(st, cond, slot) ((void)(st))
+#endif
+
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
@@ -403,12 +431,14 @@ constexpr int kMaxWaves = 16;
 
 template <int DT, int D, int WC = 0>
 __device__ __forceinline__ void wg_finish(State<Geo<DT, D>::E>& st, float (*lds_ml)[2], float* lds_o,
-                                          const DecodeArgs& a, int unit, int split) {
+                                          const DecodeArgs& a, int unit, int split,
+                                          unsigned long long* stamps = nullptr) {
   using G = Geo<DT, D>;
   constexpr int E = G::E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = WC > 0 ? WC : blockDim.x >> 6;
   const int grp = lane / G::LPR, c = lane % G::LPR;
   merge_groups<G::LPR, E>(st);
+  UOCR_STAMP(stamps, stamps && lane == 0, 56 + wave);
   if (grp == 0) {
     float4* dst = reinterpret_cast<float4*>(lds_o + wave * D + c * E);
 #pragma unroll
@@ -419,6 +449,7 @@ __device__ __forceinline__ void wg_finish(State<Geo<DT, D>::E>& st, float (*lds_
     lds_ml[wave][1] = st.l;
   }
   __syncthreads();
+  UOCR_STAMP(stamps, stamps && threadIdx.x == 0, 7);
   // every thread takes the common maximum, then output dimensions are dealt
   // to the threads; each sums the W waves' weighted partials in wave order
   // (a wave that saw no key has l = 0 and acc = 0 and adds exactly nothing)
@@ -435,7 +466,10 @@ __device__ __forceinline__ void wg_finish(State<Geo<DT, D>::E>& st, float (*lds_
   } else {
     for (int w = 0; w < W; ++w) M = fmaxf(M, lds_ml[w][0]);
   }
-  for (int t = threadIdx.x; t < D; t += blockDim.x) {
+  // the stride is a constant where the wave count is, which spares a
+  // scalar load of the launch's group size from the kernel arguments here
+  const int nth = WC > 0 ? WC * 64 : (int)blockDim.x;
+  for (int t = threadIdx.x; t < D; t += nth) {
     float L = 0.f, O = 0.f;
     if constexpr (WC > 0) {
 #pragma unroll
@@ -462,6 +496,86 @@ __device__ __forceinline__ void wg_finish(State<Geo<DT, D>::E>& st, float (*lds_
       if (t == 0) *reinterpret_cast<float2*>(a.part_ml + part * 2) = make_float2(M, L);
       a.part_o[part * D + t] = O;
     }
+  }
+}
+
+// The fused SR-SWA step's finish (W <= 8 waves, splits == 1): the row groups
+// of every wave are not merged inside the wave first; each of the
+// P = W * 64 / LPR row groups leaves its partial (max, sum, output chunk) in
+// LDS, and after one barrier the whole workgroup merges them: wave w takes
+// output dims [w * D / W, (w + 1) * D / W), TPD = 64 W / D lanes per dim,
+// each lane merging P / TPD partials, then the TPD lanes of a dim merge by
+// cross-lane swaps.  The wave that finishes last then pays for a few LDS
+// stores instead of the whole in-wave merge.  part_o (P * D floats) and
+// part_ml (P pairs) are the caller's LDS; every partial is read after the
+// barrier only.
+template <int DT, int D, int W>
+struct PartGeo {
+  static constexpr int GPW = 64 / Geo<DT, D>::LPR;  // row groups per wave
+  static constexpr int P = W * GPW;                 // partials
+  static constexpr int TPD = 64 * W / D;            // lanes per output dim
+  static constexpr int DPW = D / W;                 // dims per wave
+  static constexpr int PPT = P / TPD;               // partials per lane
+};
+
+template <int DT, int D, int W>
+__device__ __forceinline__ void wg_finish_parts(const State<Geo<DT, D>::E>& st, float* part_o, float2* part_ml,
+                                                const DecodeArgs& a, int unit,
+                                                unsigned long long* stamps = nullptr) {
+  using G = Geo<DT, D>;
+  using PG = PartGeo<DT, D, W>;
+  constexpr int E = G::E;
+  static_assert(64 * W % D == 0 && PG::P % PG::TPD == 0 && PG::DPW * PG::TPD == 64, "finish geometry");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / G::LPR, c = lane % G::LPR;
+  const int p = wave * PG::GPW + grp;
+  float4* dst = reinterpret_cast<float4*>(part_o + p * D + c * E);
+#pragma unroll
+  for (int e = 0; e < E; e += 4) dst[e / 4] = make_float4(st.acc[e], st.acc[e + 1], st.acc[e + 2], st.acc[e + 3]);
+  if (c == 0) part_ml[p] = make_float2(st.m, st.l);
+  UOCR_STAMP(stamps, stamps && lane == 0, 56 + wave);
+  __syncthreads();
+  UOCR_STAMP(stamps, stamps && threadIdx.x == 0, 7);
+  // lane (qq, dl) of wave w: dim d = w * DPW + dl, partials qq, qq + TPD, ...
+  const int dl = lane % PG::DPW, qq = lane / PG::DPW, d = wave * PG::DPW + dl;
+  float mw[PG::PPT];
+  float M = kFloor;
+#pragma unroll
+  for (int i = 0; i < PG::PPT; ++i) {
+    mw[i] = part_ml[i * PG::TPD + qq].x;
+    M = fmaxf(M, mw[i]);
+  }
+  float L = 0.f, O = 0.f;
+#pragma unroll
+  for (int i = 0; i < PG::PPT; ++i) {
+    const int pi = i * PG::TPD + qq;
+    const float f = fexp2(mw[i] - M);
+    L = fmaf(f, part_ml[pi].y, L);
+    O = fmaf(f, part_o[pi * D + d], O);
+  }
+#pragma unroll
+  for (int off = PG::DPW; off < 64; off *= 2) {
+    float mo, lo, oo;
+    if (off == 16) {
+      mo = xor16(M), lo = xor16(L), oo = xor16(O);
+    } else if (off == 32) {
+      mo = xor32(M), lo = xor32(L), oo = xor32(O);
+    } else {
+      mo = __shfl_xor(M, off), lo = __shfl_xor(L, off), oo = __shfl_xor(O, off);
+    }
+    const float mn = fmaxf(M, mo);
+    const float fa = fexp2(M - mn), fb = fexp2(mo - mn);
+    L = L * fa + lo * fb;
+    O = O * fa + oo * fb;
+    M = mn;
+  }
+  if (qq == 0) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    char* dst_row = static_cast<char*>(a.out) + (size_t)unit * G::ROWB;
+    if constexpr (DT == 0)
+      reinterpret_cast<float*>(dst_row)[d] = O * inv;
+    else
+      reinterpret_cast<uint16_t*>(dst_row)[d] = (uint16_t)bf16_bits(O * inv);
   }
 }
 
@@ -2098,7 +2212,7 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   constexpr int SL = NT / kIdxDim;  // slices of D in the q_idx product
   constexpr int KB = 4;             // block keys loaded per thread per batch
   constexpr int RPP = NT / 8;       // block keys per pass (8 lanes per key)
-  __shared__ float s_scores[kMaxBlocks];
+  __shared__ __attribute__((aligned(16))) float s_scores[kMaxBlocks];
   __shared__ double s_red[SL][kIdxDim];
   __shared__ __attribute__((aligned(16))) double s_qidx[kIdxDim];
   __shared__ TopkSmem<NT> tsm;
@@ -2107,12 +2221,24 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   __shared__ float lds_ml[W][2];
   __shared__ __attribute__((aligned(16))) float lds_o[W * D];
   __shared__ __attribute__((aligned(16))) float s_q[D];  // the rotated q (page2d RoPE only)
+  // the finish's partial pairs (the partial outputs reuse s_scores, which no
+  // wave reads once it has the selection)
+  constexpr bool kParts = W <= 8 && PartGeo<DT, D, W>::P * D <= kMaxBlocks;
+  __shared__ float2 s_pml[kParts ? PartGeo<DT, D, W>::P : 1];
+  UOCR_STAMP_LDS;
   const DecodeArgs& d = a.d;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x, b = unit / d.heads, h = unit - b * d.heads;
   const bool rope = a.rope_page != nullptr;
   const int grp = lane / G::LPR, c = lane % G::LPR;
   const size_t cb = (size_t)c * 16;
+  UOCR_STAMP(s_stamp, tid == 0, 0);
+#ifdef UOCR_PHASE_STAMPS
+  if (tid == 0) {
+    s_stamp[3] = __builtin_amdgcn_s_getreg((3 << 11) | 20);   // XCC_ID: the XCD
+    s_stamp[8] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID: CU, shader array, engine
+  }
+#endif
 
   // The loads that depend on nothing but the unit go out first, in order:
   // the new token's row (stored into its ring slot once the count is known),
@@ -2209,6 +2335,7 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
     s_qidx[tid] = sum;
   }
   __syncthreads();
+  UOCR_STAMP(s_stamp, tid == 0, 5);
 
   // block scores (fp64 dot products, rounded once to fp32) into LDS; the
   // next batch of keys is loaded while the current one is scored
@@ -2229,12 +2356,14 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
     constexpr int BATCH = RPP * KB;
     for (int jb = 0; jb < nb; jb += 2 * BATCH) {
       score(kvA, jb);
+      UOCR_STAMP(s_stamp, jb == 0 && tid == 0, 6);
       if (jb + 2 * BATCH < nb) load_keys(kvA, jb + 2 * BATCH);
       score(kvB, jb + BATCH);
       if (jb + 3 * BATCH < nb) load_keys(kvB, jb + 3 * BATCH);
     }
   }
   __syncthreads();
+  UOCR_STAMP(s_stamp, tid == 0, 1);
 
   // Window attention on waves 1 .. W-1 while wave 0 routes: every slot of
   // the ring is addressable, so each of these waves reads its share of all n
@@ -2252,6 +2381,7 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
                                       rope ? -1 : slot - r0, static_cast<const char*>(a.k_new) + nbase,
                                       static_cast<const char*>(a.v_new) + nbase, w - r0);
     }
+    UOCR_STAMP_DONE(s_stamp, lane == 0, 16 + wave);
   };
   const size_t so = (size_t)unit * d.topk;
   const bool bar = entmax_topk_block<NT, decltype(window), true>(
@@ -2261,6 +2391,7 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
     __syncthreads();
   else
     wait_flag(&tsm.flag);
+  UOCR_STAMP(s_stamp, lane == 0, wave == 0 ? 2 : 32 + wave);
 
   // Live selected blocks, as tasks of 32 / cpb rows; task i goes to wave
   // i mod W, which starts on it as soon as it has the selection: wave 0 right
@@ -2296,7 +2427,16 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
     attend_fit<DT, D, STREAM>(static_cast<const char*>(d.k_prefix) + base,
                               static_cast<const char*>(d.v_prefix) + base, nr, bj * kLog2e, q, st, grp);
   }
-  wg_finish<DT, D, W>(st, lds_ml, lds_o, d, unit, 0);
+  UOCR_STAMP_DONE(s_stamp, lane == 0, 48 + wave);
+  if constexpr (kParts)
+    wg_finish_parts<DT, D, W>(st, s_scores, s_pml, d, unit, s_stamp);
+  else
+    wg_finish<DT, D, W>(st, lds_ml, lds_o, d, unit, 0, s_stamp);
+#ifdef UOCR_PHASE_STAMPS
+  if (tid == 0) s_stamp[4] = wall_clock64();
+  __syncthreads();
+  if (tid < kStampSlots && unit < kMaxStampUnits) g_stamps[(size_t)unit * kStampSlots + tid] = s_stamp[tid];
+#endif
 }
 
 // uocr_rswa_step: the dense decode with the append fused in.  Every
@@ -2653,6 +2793,20 @@ hipError_t launch_rswa_step(int dtype, int head_dim, const StepArgs& a, hipStrea
   if (e != hipSuccess || a.d.splits == 1) return e;
   UOCR_DISPATCH(k_split_merge, dim3((unsigned)((a.d.units + 3) / 4)), dim3(256), a.d);
   return hipGetLastError();
+}
+
+hipError_t read_phase_stamps(void* dst, size_t bytes, hipStream_t s) {
+#ifdef UOCR_PHASE_STAMPS
+  if (bytes > sizeof(g_stamps)) return hipErrorInvalidValue;
+  hipError_t e = hipMemcpyFromSymbolAsync(dst, HIP_SYMBOL(g_stamps), bytes, 0, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(s);
+#else
+  (void)dst;
+  (void)bytes;
+  (void)s;
+  return hipErrorNotSupported;
+#endif
 }
 
 }  // namespace uocr

@@ -16,10 +16,13 @@ import math
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libuocr.so")
+# the same sources with the fused SR-SWA step's phase stamps compiled in
+STAMPS_LIB_PATH = os.path.join(_HERE, "libuocr_stamps.so")
 
 UOCR_F32, UOCR_BF16 = 0, 1
 _TORCH_DTYPE = {UOCR_F32: torch.float32, UOCR_BF16: torch.bfloat16}
@@ -96,21 +99,33 @@ class Route:
 
 
 _lib = None
+_lib_path = LIB_PATH
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
 
 
+def use_phase_stamps() -> None:
+    """Make this process load libuocr_stamps.so instead of libuocr.so: the
+    same entry points, with the fused SR-SWA step recording its phase stamps
+    (read with uocr_phase_stamps).  Must come before the first call."""
+    global _lib_path
+    if _lib is not None and _lib_path != STAMPS_LIB_PATH:
+        raise RuntimeError("libuocr.so is already loaded in this process")
+    _lib_path = STAMPS_LIB_PATH
+
+
 def load_library():
-    """Load libuocr.so (once).  torch is imported first so that the process
-    has a single HIP runtime.  Raises if the library has not been built."""
+    """Load libuocr.so (once; libuocr_stamps.so after use_phase_stamps()).
+    torch is imported first so that the process has a single HIP runtime.
+    Raises if the library has not been built."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+    if not os.path.exists(_lib_path):
+        raise RuntimeError(f"{_lib_path} is missing: build it with "
                            "`python -m long_context_decode_attn_amd.build` (needs hipcc)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(_lib_path)
     SP, RP = ctypes.POINTER(_Shape), ctypes.POINTER(_Route)
     sig = {
         "uocr_ring_append": (ctypes.c_int, [SP, _P, _P, _P, _P, _P, _P]),
@@ -137,6 +152,7 @@ def load_library():
         "uocr_calib_pull": (ctypes.c_int, [_P, _SZ, _I32, _I32, _I32, _P, _P]),
         "uocr_calib_start": (ctypes.c_int, [_I32, _I32, _P, _P]),
         "uocr_calib_exchange": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, _P, _P]),
+        "uocr_phase_stamps": (ctypes.c_int, [_P, _I32, _P]),
         "uocr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "uocr_last_error": (ctypes.c_char_p, []),
         "uocr_version": (ctypes.c_int, []),
@@ -154,7 +170,8 @@ EXPORTED = ("uocr_ring_append", "uocr_rswa_splits", "uocr_rswa_workspace_bytes",
             "uocr_prefill_route", "uocr_ngram_ban", "uocr_rope_page2d",
             "uocr_srswa_splits", "uocr_srswa_workspace_bytes", "uocr_srswa_decode", "uocr_rswa_step", "uocr_srswa_step",
             "uocr_status_string", "uocr_last_error", "uocr_version",
-            "uocr_calib_read", "uocr_calib_empty", "uocr_calib_pull", "uocr_calib_start", "uocr_calib_exchange")
+            "uocr_calib_read", "uocr_calib_empty", "uocr_calib_pull", "uocr_calib_start", "uocr_calib_exchange",
+            "uocr_phase_stamps")
 
 
 # ----------------------------------------------------------------------------
@@ -468,6 +485,17 @@ def uocr_calib_exchange(mode: int, units: int, split: int, part: torch.Tensor, c
     _check(count, "count", torch.int32, (units,))
     _check(out, "out", torch.float32, (units * 130,))
     _calib_call("uocr_calib_exchange", mode, units, split, _ptr(part), _ptr(count), _ptr(out), _stream(stream))
+
+
+def uocr_phase_stamps(units: int, stream=None) -> np.ndarray:
+    """The phase stamps of units [0, units) of the latest fused SR-SWA steps,
+    [units][64] uint64 (slots as in include/uocr_calib.h); raises UocrError
+    (UOCR_ERR_UNSUPPORTED) unless use_phase_stamps() came first."""
+    out = np.zeros((units, 64), dtype=np.uint64)
+    rc = load_library().uocr_phase_stamps(ctypes.c_void_p(out.ctypes.data), int(units), _stream(stream))
+    if rc != 0:
+        raise UocrError("uocr_phase_stamps", rc, uocr_last_error())
+    return out
 
 
 def uocr_version() -> int:

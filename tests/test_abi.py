@@ -234,3 +234,23 @@ def test_static_workspace_refuses_a_split_count_that_does_not_fit():
                                        None) == -1
     assert lib.uocr_rswa_decode_static(ctypes.byref(_shape(U)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1,
                                        None) == -2
+
+
+def test_phase_stamps_only_in_the_stamping_library():
+    """uocr_phase_stamps: libuocr.so records no stamps and says so (before
+    any HIP call); libuocr_stamps.so, built from the same sources with the
+    stamps compiled in, exports the same entry points."""
+    import numpy as np
+    U, lib = _lib()
+    buf = np.zeros((4, 64), dtype=np.uint64)
+    p = ctypes.c_void_p(buf.ctypes.data)
+    assert lib.uocr_phase_stamps(None, 4, None) == -1
+    assert lib.uocr_phase_stamps(p, 0, None) == -2
+    assert lib.uocr_phase_stamps(p, 4097, None) == -2
+    assert lib.uocr_phase_stamps(p, 4, None) == -6
+    assert "libuocr_stamps.so" in lib.uocr_last_error().decode()
+    if not os.path.exists(U.STAMPS_LIB_PATH):
+        pytest.skip("libuocr_stamps.so is not built in this checkout")
+    stamped = ctypes.CDLL(U.STAMPS_LIB_PATH)
+    for n in _declared():
+        assert hasattr(stamped, n), n
