@@ -709,6 +709,12 @@ def phases_main(args):
         "cus_used": int(len(cnt)), "units_on_shared_cus": int(shared.sum()),
         "end_us_alone": _quantiles(life[:, ~shared]) if (~shared).any() else None,
         "end_us_shared": _quantiles(life[:, shared]) if shared.any() else None,
+        "shared_vs_alone_p50_us": {
+            k: [round(float(np.median(v[:, ~shared])), 3) if (~shared).any() else None,
+                round(float(np.median(v[:, shared])), 3) if shared.any() else None]
+            for k, v in (("q_idx", t[:, :, 5] - t0), ("scores_in_lds", t[:, :, 1] - t0),
+                         ("routed", t[:, :, 2] - t0), ("window_done", win - t0), ("live_done", live - t0),
+                         ("end", life))},
         "units_per_xcd": np.bincount(xcc.astype(np.int64), minlength=8).tolist(),
         "start_us_p50_by_xcd": [round(float(np.median(t0[:, xcc == k])), 3) if (xcc == k).any() else None
                                 for k in range(8)],
