@@ -39,15 +39,15 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("79ab4e0c72fb3432", 45186684, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("79ab4e0c72fb3432", 18909846, 76928),
-    ("uocr_srswa_step", "srswa-40p-b32-wide"): ("79ab4e0c72fb3432", 118624123, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8-wide"): ("79ab4e0c72fb3432", 37066603, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("79ab4e0c72fb3432", 892113006, 1024674),
-    ("uocr_rswa_step", "dense-1p-b512"): ("79ab4e0c72fb3432", 1092754718, 3940448),
-    ("uocr_rswa_step", "dense-40p-b32"): ("79ab4e0c72fb3432", 1699107151, 686881),
-    ("uocr_rswa_step", "dense-125p-b8"): ("79ab4e0c72fb3432", 1316158628, 302180),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("79ab4e0c72fb3432", 169068478, 167790668),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("d6c664b40684f2c3", 45143758, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("d6c664b40684f2c3", 18887308, 76928),
+    ("uocr_srswa_step", "srswa-40p-b32-wide"): ("d6c664b40684f2c3", 118582850, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8-wide"): ("d6c664b40684f2c3", 37045255, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("d6c664b40684f2c3", 892116327, 1024694),
+    ("uocr_rswa_step", "dense-1p-b512"): ("d6c664b40684f2c3", 1092751760, 3940452),
+    ("uocr_rswa_step", "dense-40p-b32"): ("d6c664b40684f2c3", 1699114003, 686830),
+    ("uocr_rswa_step", "dense-125p-b8"): ("d6c664b40684f2c3", 1316159537, 302175),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("d6c664b40684f2c3", 169090737, 167785592),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
@@ -703,6 +703,10 @@ def phases_main(args):
         "merge_barrier_us": _quantiles(t[:, :, 7] - t0),
         "end_us": _quantiles(life),
         "routing_us": _quantiles(t[:, :, 2] - t[:, :, 1]),
+        # inside the routing (one-wave path): max, threshold, compaction, ranks, entmax, outputs
+        "routing_parts_us": [round(float(np.median(b - a)), 3) for a, b in
+                             ((t[:, :, 1], t[:, :, 9]), (t[:, :, 9], t[:, :, 10]), (t[:, :, 10], t[:, :, 11]),
+                              (t[:, :, 11], t[:, :, 12]), (t[:, :, 12], t[:, :, 13]), (t[:, :, 13], t[:, :, 2]))],
         "window_after_scores_us": _quantiles(win - t[:, :, 1]),
         "live_after_routing_us": _quantiles(live - np.maximum(t[:, :, 2], win)),
         "finish_us": _quantiles(end - live),

@@ -93,6 +93,10 @@ int uocr_calib_exchange(int32_t mode, int32_t units, int32_t split, float* part,
  *  56+w wave w has left its share of the merge in LDS
  *   7 the workgroup merge's barrier has passed
  *   4 the output row is written
+ *   9-13 inside the routing of wave 0 (one-wave path only): 9 the scores'
+ *     maximum taken, 10 the threshold of the candidate set A found, 11 A
+ *     compacted (and its rank keys and the entmax candidates in LDS),
+ *     12 ranks counted, 13 the entmax threshold found
  *   3 (not a time) the XCD the workgroup ran on (hardware register XCC_ID)
  *   8 (not a time) hardware register HW_ID of wave 0: bits 8-11 the compute
  *     unit, 12 the shader array, 13-15 the shader engine within the XCD

@@ -1160,7 +1160,8 @@ __device__ __forceinline__ double wave_sum_d(double x) {
 // u <= tau_S off S), which single out the exact support.
 template <int NS, bool WIDE = false>
 __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32_t* o_idx, float* o_prob,
-                                           float* o_bias, int* l_idx, float* l_bias, PairBuf& pb) {
+                                           float* o_bias, int* l_idx, float* l_bias, PairBuf& pb,
+                                           unsigned long long* stamps = nullptr) {
   const int lane = threadIdx.x & 63;
   // the routing is the critical path of the step: let this wave win the
   // issue arbitration against the waves attending over the window
@@ -1175,6 +1176,7 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
     if constexpr (WIDE) lmin = j < nb ? fminf(lmin, sv[e]) : lmin;
   }
   const float smax = wave_max(lmax);
+  UOCR_STAMP(stamps, stamps && lane == 0, 9);
   // WIDE: the largest gap smax - s of a visible block (the searches below
   // start from it when the support is wide)
   const float dlast = WIDE ? smax + wave_max(-lmin) : 0.f;
@@ -1236,35 +1238,89 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
       }
     }
   }
+  UOCR_STAMP(stamps, stamps && lane == 0, 10);
   if (nA <= 64) {
-    // ordered compaction of A (and of the entmax candidates) by ballots
-    int base = 0, cbase = 0;
-#pragma unroll
-    for (int e = 0; e < NS; ++e) {
-      const bool in = dv[e] < T;
-      const bool cd = !wide && ((double)sv[e] - dmax) * 0.5 > -1.0;
-      const uint64_t m = __ballot(in);
-      const uint64_t mc = __ballot(cd);
-      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const int cbelow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
-      if (in) pb.key[base + below] = rank_key(sv[e], e * 64 + lane);
-      if (cd) pb.rank[cbase + cbelow] = __float_as_int(sv[e]);  // candidate scores
-      base += __popcll(m);
-      cbase += __popcll(mc);
-    }
-    const int nC = cbase;
-    const int nA4 = (nA + 3) & ~3, nC4 = (nC + 3) & ~3;
-    if (lane < nA4 - nA) pb.key[nA + lane] = 0;  // below every block's key
-    if (lane < nC4 - nC) pb.rank[nC + lane] = __float_as_int(-INFINITY);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Ordered compaction of A by ballots (slot-major order is index order).
+    // Two ways, with identical results (A, its rank keys and the candidate
+    // list in index order):
+    //  - PAIRS (prefill, and the decode step at more than 512 blocks): only
+    //    (index, score bits) pairs per slot; afterwards each lane of A forms
+    //    its rank key and the entmax candidates (d < 2, all in A) are
+    //    compacted from the lanes, a third of the per-slot instructions;
+    //  - otherwise keys and candidate scores per slot.  At up to 512 blocks
+    //    the window, not the routing, is the longer branch of the step, and
+    //    a routing wave that finished sooner started its live blocks while
+    //    the window was still streaming: 40 pages got slower.
+    constexpr bool PAIRS = WIDE || NS >= 16;
+    const int nA4 = (nA + 3) & ~3;
     const bool mine = lane < nA;
-    const uint64_t ki = mine ? pb.key[lane] : 0;
-    const float si = mine ? rank_key_score(ki) : -INFINITY;
-    const int ii = (int)~(uint32_t)ki;
-    const double vi = ((double)si - dmax) * 0.5;
+    int nC, ii;
+    uint64_t ki;
+    float si;
+    double vi;
+    if constexpr (PAIRS) {
+      int base = 0;
+#pragma unroll
+      for (int e = 0; e < NS; ++e) {
+        const bool in = dv[e] < T;
+        const uint64_t m = __ballot(in);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (in) pb.key[base + below] = ((uint64_t)(uint32_t)(e * 64 + lane) << 32) | __float_as_uint(sv[e]);
+        base += __popcll(m);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint64_t pr = mine ? pb.key[lane] : 0;
+      ii = (int)(uint32_t)(pr >> 32);
+      const float sraw = __uint_as_float((uint32_t)pr);
+      ki = mine ? rank_key(sraw, ii) : 0;
+      si = mine ? rank_key_score(ki) : -INFINITY;
+      vi = ((double)si - dmax) * 0.5;
+      // each lane's rank key (0 past nA: below every block's key), and the
+      // candidates' scores in A's order, padded as below
+      const bool cd = !wide && mine && vi > -1.0;
+      const uint64_t mc = __ballot(cd);
+      nC = __popcll(mc);
+      const int nC4 = (nC + 3) & ~3;
+      if (lane < nA4) pb.key[lane] = ki;
+      if (cd)
+        pb.rank[__builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u))] =
+            __float_as_int(sraw);
+      if (lane >= nC && lane < nC4) pb.rank[lane] = __float_as_int(-INFINITY);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      int base = 0, cbase = 0;
+#pragma unroll
+      for (int e = 0; e < NS; ++e) {
+        const bool in = dv[e] < T;
+        const bool cd = !wide && ((double)sv[e] - dmax) * 0.5 > -1.0;
+        const uint64_t m = __ballot(in);
+        const uint64_t mc = __ballot(cd);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const int cbelow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
+        if (in) pb.key[base + below] = rank_key(sv[e], e * 64 + lane);
+        if (cd) pb.rank[cbase + cbelow] = __float_as_int(sv[e]);  // candidate scores
+        base += __popcll(m);
+        cbase += __popcll(mc);
+      }
+      nC = cbase;
+      const int nC4 = (nC + 3) & ~3;
+      if (lane < nA4 - nA) pb.key[nA + lane] = 0;  // below every block's key
+      if (lane < nC4 - nC) pb.rank[nC + lane] = __float_as_int(-INFINITY);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      ki = mine ? pb.key[lane] : 0;
+      si = mine ? rank_key_score(ki) : -INFINITY;
+      ii = (int)~(uint32_t)ki;
+      vi = ((double)si - dmax) * 0.5;
+    }
+    const int nC4 = (nC + 3) & ~3;
+    UOCR_STAMP(stamps, stamps && lane == 0, 11);
     const ulonglong2* key2 = reinterpret_cast<const ulonglong2*>(pb.key);
     int rank = 0;  // blocks of A ahead of this lane's in (score desc, index asc)
     auto rank4 = [&](int k4) {
@@ -1278,6 +1334,7 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
 #pragma unroll 2
       for (int k4 = 0; k4 < nA4 / 4; ++k4) rank4(k4);
     }
+    UOCR_STAMP(stamps, stamps && lane == 0, 12);
     double tau;
     if (!wide) {
       const bool cand = mine && vi > -1.0;
@@ -1351,6 +1408,7 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
         return false;
       }
     }
+    UOCR_STAMP(stamps, stamps && lane == 0, 13);
     const bool sel = mine && rank < kk;
     const uint64_t sm_ = __ballot(sel);
     if (sel) {
@@ -1389,7 +1447,7 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
 template <int NT, typename F = NoOverlap, bool EARLY = false>
 __device__ __forceinline__ bool entmax_topk_block(const float* s, int nb, int topk, int32_t* o_idx, float* o_prob,
                                   float* o_bias, int* l_idx, float* l_bias, TopkSmem<NT>& sm,
-                                  const F& others = F()) {
+                                  const F& others = F(), unsigned long long* stamps = nullptr) {
   constexpr int PT = kMaxBlocks / NT;  // values per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kk = min(topk, nb);
@@ -1425,11 +1483,11 @@ __device__ __forceinline__ bool entmax_topk_block(const float* s, int nb, int to
     if (wave != 0) others();
     bool ok = false;
     if (wave == 0) {
-      if (nb <= 64) ok = wave_route<1>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
-      else if (nb <= 128) ok = wave_route<2>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
-      else if (nb <= 256) ok = wave_route<4>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
-      else if (nb <= 512) ok = wave_route<8>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
-      else ok = wave_route<16>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a);
+      if (nb <= 64) ok = wave_route<1>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a, stamps);
+      else if (nb <= 128) ok = wave_route<2>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a, stamps);
+      else if (nb <= 256) ok = wave_route<4>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a, stamps);
+      else if (nb <= 512) ok = wave_route<8>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a, stamps);
+      else ok = wave_route<16>(s, nb, kk, o_idx, o_prob, o_bias, l_idx, l_bias, sm.a, stamps);
     }
     if constexpr (EARLY) {
       // 1: selection published; 2: the workgroup path below takes over
@@ -2386,7 +2444,7 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   const size_t so = (size_t)unit * d.topk;
   const bool bar = entmax_topk_block<NT, decltype(window), true>(
       s_scores, nb, d.topk, a.sel_idx + so, a.sel_prob ? a.sel_prob + so : nullptr, a.sel_bias + so, l_idx,
-      l_bias, tsm, window);
+      l_bias, tsm, window, s_stamp);
   if (bar)
     __syncthreads();
   else
