@@ -2278,7 +2278,7 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   __shared__ float l_bias[kMaxTopk];
   __shared__ float lds_ml[W][2];
   __shared__ __attribute__((aligned(16))) float lds_o[W * D];
-  __shared__ __attribute__((aligned(16))) float s_q[D];  // the rotated q (page2d RoPE only)
+  __shared__ __attribute__((aligned(16))) float s_q[D];  // q (turned by page2d RoPE if asked)
   // the finish's partial pairs (the partial outputs reuse s_scores, which no
   // wave reads once it has the selection)
   constexpr bool kParts = W <= 8 && PartGeo<DT, D, W>::P * D <= kMaxBlocks;
@@ -2309,22 +2309,16 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
       ld16(static_cast<const char*>(a_which ? a.v_new : a.k_new) + (size_t)unit * G::ROWB + a_off * 16);
 
   // q_idx partial sums: the loads of P and q go out first, so that they are
-  // not queued behind the block keys
+  // not queued behind the block keys.  q is loaded once, one element per
+  // thread of the first D, and shared through LDS (s_q) with the q_idx
+  // product and the attention, instead of every thread loading its share
+  // twice: fewer loads through the CU's memory pipeline in front of the keys.
   const int i_q = tid % kIdxDim, sl_q = tid / kIdxDim;
   constexpr int DPS = D / SL;
   float pv[DPS], qv_[DPS];
-  {
-    const char* qrow = static_cast<const char*>(d.q) + (size_t)unit * G::ROWB;
 #pragma unroll
-    for (int k = 0; k < DPS; ++k) {
-      const int dd = sl_q * DPS + k;
-      pv[k] = a.proj[dd * kIdxDim + i_q];
-      if constexpr (DT == 0)
-        qv_[k] = reinterpret_cast<const float*>(qrow)[dd];
-      else
-        qv_[k] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qrow)[dd] << 16);
-    }
-  }
+  for (int k = 0; k < DPS; ++k) pv[k] = a.proj[(sl_q * DPS + k) * kIdxDim + i_q];
+  const float qe = tid < D ? row_elem<DT>(static_cast<const char*>(d.q) + (size_t)unit * G::ROWB, tid) : 0.f;
 
   // the first two batches of block keys (rows < nb_cap: no wait for
   // prefix_len), in flight while q_idx is formed.  The loads are
@@ -2352,15 +2346,16 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   const int n = d.window, slot = t % n, w = min(n, t + 1);
   const int nb = (m + kBlock - 1) / kBlock;
 
-  // page2d RoPE: q is turned into s_q and the turned k_new row written into
-  // its ring slot (pair-wise), before anything reads them; the block keys'
-  // loads are already in flight
-  if (rope) {
+  // q into s_q; with page2d RoPE turned on the way, and the turned k_new row
+  // written into its ring slot (pair-wise), before anything reads them.  The
+  // block keys' loads are already in flight.
+  if (rope)
     step_rope<DT, D>(a, unit, b, s_q, static_cast<char*>(a.k_ring) + ((size_t)unit * n + slot) * G::ROWB);
-    __syncthreads();
+  else if (tid < D)
+    s_q[tid] = qe;
+  __syncthreads();
 #pragma unroll
-    for (int k = 0; k < DPS; ++k) qv_[k] = s_q[sl_q * DPS + k];
-  }
+  for (int k = 0; k < DPS; ++k) qv_[k] = s_q[sl_q * DPS + k];
   {
     double acc = 0.0;
 #pragma unroll
@@ -2377,12 +2372,8 @@ __global__ __launch_bounds__(NT, NT >= 512 ? 4 : 3) void k_srswa_step(StepArgs a
   if (tid == 0) tsm.flag = 0;  // zeroed before the first workgroup barrier
 
   float q[G::E];
-  if (rope) {
 #pragma unroll
-    for (int e = 0; e < G::E; ++e) q[e] = s_q[c * G::E + e] * d.qscale;
-  } else {
-    load_q<DT, D>(d.q, unit, c, d.qscale, q);
-  }
+  for (int e = 0; e < G::E; ++e) q[e] = s_q[c * G::E + e] * d.qscale;
   State<G::E> st;
   st.init();
   __syncthreads();
