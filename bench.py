@@ -39,15 +39,15 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("d6c664b40684f2c3", 45143758, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("d6c664b40684f2c3", 18887308, 76928),
-    ("uocr_srswa_step", "srswa-40p-b32-wide"): ("d6c664b40684f2c3", 118582850, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8-wide"): ("d6c664b40684f2c3", 37045255, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("d6c664b40684f2c3", 892116327, 1024694),
-    ("uocr_rswa_step", "dense-1p-b512"): ("d6c664b40684f2c3", 1092751760, 3940452),
-    ("uocr_rswa_step", "dense-40p-b32"): ("d6c664b40684f2c3", 1699114003, 686830),
-    ("uocr_rswa_step", "dense-125p-b8"): ("d6c664b40684f2c3", 1316159537, 302175),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("d6c664b40684f2c3", 169090737, 167785592),
+    ("uocr_srswa_step", "srswa-40p-b32"): ("71e94db68c2090ee", 45191748, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8"): ("71e94db68c2090ee", 18909782, 76928),
+    ("uocr_srswa_step", "srswa-40p-b32-wide"): ("71e94db68c2090ee", 118623855, 307712),
+    ("uocr_srswa_step", "srswa-125p-b8-wide"): ("71e94db68c2090ee", 37067772, 76928),
+    ("uocr_rswa_step", "dense-10p-b64"): ("71e94db68c2090ee", 892089286, 1024677),
+    ("uocr_rswa_step", "dense-1p-b512"): ("71e94db68c2090ee", 1092735344, 3940450),
+    ("uocr_rswa_step", "dense-40p-b32"): ("71e94db68c2090ee", 1699103287, 686877),
+    ("uocr_rswa_step", "dense-125p-b8"): ("71e94db68c2090ee", 1316148344, 302168),
+    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("71e94db68c2090ee", 169091256, 167782557),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"
