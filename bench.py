@@ -93,7 +93,7 @@ def parse():
 
 
 # ----------------------------------------------------------------------------
-# algorithmic bytes per launch (what each kernel must move)
+# algorithmic bytes per launch: what each kernel must read and write
 # ----------------------------------------------------------------------------
 def algorithmic_bytes(w, live_blocks_per_unit=None):
     """Bytes each kernel must read + write per launch for the workload."""
@@ -748,7 +748,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode path has no "
-              f"cross-GPU step; see DESIGN.md for how it would shard.", file=sys.stderr)
+              f"cross-GPU step: sequences (and heads) split across GPUs with no communication.",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate:
