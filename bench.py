@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--t0", type=int, default=None,
                     help="generated tokens before the first step (default: the workload's; for flatness runs)")
+    ap.add_argument("--pages", type=int, default=None,
+                    help="prefix pages of 256 tokens instead of the workload's (document-length sweeps)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="sequences instead of the workload's (document-length sweeps)")
     ap.add_argument("--mode", choices=["fused", "separate"], default="fused",
                     help="fused: one uocr_*_step launch per step; separate: one launch per row")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
@@ -767,6 +771,12 @@ def main():
     w = S.WORKLOADS[args.workload]
     if args.t0 is not None:
         w = w.replace(t0=args.t0)
+    if args.pages is not None or args.batch is not None:
+        pages = w.pages if args.pages is None else args.pages
+        batch = w.batch if args.batch is None else args.batch
+        if pages < 1 or batch < 1 or (w.sparse and pages * S.TOKENS_PER_PAGE // w.block < w.planted):
+            sys.exit(f"--pages {pages} --batch {batch}: out of range for {w.name}")
+        w = w.replace(name=f"{w.name}@{pages}p-b{batch}", pages=pages, batch=batch)
     # the CPU baseline forks its worker processes before anything touches the GPU
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
 
