@@ -21,6 +21,28 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
+def test_document_length_override_refuses_a_prefix_without_room_for_the_planted_blocks():
+    # 1 page holds 8 blocks, fewer than the 16 planted ones of the 40-page workload
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "srswa-40p-b32", "--pages",
+                        "1", "--batch", "8", "--no-cpu-baseline"], capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "out of range" in r.stderr and r.stdout == ""
+
+
+def test_document_length_override_bytes_scale_with_the_pages():
+    """The dense step's bytes follow the prefix; the sparse step's block keys
+    follow it at 128 B per 32 tokens while its window and selected blocks do not."""
+    w = S.WORKLOADS["dense-40p-b32"]
+    small, big = w.replace(pages=2, batch=8), w.replace(pages=125, batch=8)
+    d = lambda x: bench.algorithmic_bytes(x)["uocr_rswa_decode"] / x.units
+    assert d(big) - d(small) == (125 - 2) * 256 * 2 * 128 * 2
+    ws = S.WORKLOADS["srswa-40p-b32"]
+    ss, sb = ws.replace(pages=2, batch=8), ws.replace(pages=125, batch=8)
+    keys = lambda x: bench.algorithmic_bytes(x)["uocr_block_score"] / x.units
+    assert abs((keys(sb) - keys(ss)) - (sb.n_blocks - ss.n_blocks) * 128) <= 8 * (sb.n_blocks - ss.n_blocks)
+    sd = lambda x: bench.algorithmic_bytes(x)["uocr_srswa_decode"] / x.units
+    assert sd(sb) == sd(ss)
+
+
 # bytes per unit per step: append 1,024 B; dense decode q + 2 (m + w) D 2 + out;
 # sparse decode q + selection + 2 (512 + w) D 2 + out = 328,320 B
 @pytest.mark.parametrize("name,per_unit,kernel", [
