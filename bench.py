@@ -39,15 +39,15 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published
 # uocr_kernels.hip); otherwise the traffic is reported as null.
 COUNTER_TRAFFIC = {
     # (kernel, workload): (kernel source sha256[:16], fetch bytes, write bytes)
-    ("uocr_srswa_step", "srswa-40p-b32"): ("71e94db68c2090ee", 45191748, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8"): ("71e94db68c2090ee", 18909782, 76928),
-    ("uocr_srswa_step", "srswa-40p-b32-wide"): ("71e94db68c2090ee", 118623855, 307712),
-    ("uocr_srswa_step", "srswa-125p-b8-wide"): ("71e94db68c2090ee", 37067772, 76928),
-    ("uocr_rswa_step", "dense-10p-b64"): ("71e94db68c2090ee", 892089286, 1024677),
-    ("uocr_rswa_step", "dense-1p-b512"): ("71e94db68c2090ee", 1092735344, 3940450),
-    ("uocr_rswa_step", "dense-40p-b32"): ("71e94db68c2090ee", 1699103287, 686877),
-    ("uocr_rswa_step", "dense-125p-b8"): ("71e94db68c2090ee", 1316148344, 302168),
-    ("uocr_rope_page2d", "srswa-40p-b32-rope-chunk2048"): ("71e94db68c2090ee", 169091256, 167782557),
+    ('uocr_srswa_step', 'srswa-40p-b32'): ('d95115f5fa62f511', 45176646, 307712),
+    ('uocr_srswa_step', 'srswa-125p-b8'): ('d95115f5fa62f511', 18890109, 76928),
+    ('uocr_srswa_step', 'srswa-40p-b32-wide'): ('d95115f5fa62f511', 118613853, 307712),
+    ('uocr_srswa_step', 'srswa-125p-b8-wide'): ('d95115f5fa62f511', 37049953, 76928),
+    ('uocr_rswa_step', 'dense-10p-b64'): ('d95115f5fa62f511', 892108762, 1024667),
+    ('uocr_rswa_step', 'dense-1p-b512'): ('d95115f5fa62f511', 1092732502, 3940448),
+    ('uocr_rswa_step', 'dense-40p-b32'): ('d95115f5fa62f511', 1699100325, 686845),
+    ('uocr_rswa_step', 'dense-125p-b8'): ('d95115f5fa62f511', 1316147184, 302165),
+    ('uocr_rope_page2d', 'srswa-40p-b32-rope-chunk2048'): ('d95115f5fa62f511', 169090846, 167781105),
 }
 METRIC = "decode attn steps/s (batch×heads) + achieved HBM GB/s vs peak at 40 pages"
 UNIT = "steps/s (batch×heads)"

@@ -1043,6 +1043,15 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 constexpr int kPairMax = 256;  // largest candidate set ranked pairwise
 constexpr int kWaveBlocks = 16; // blocks per lane on the one-wave path (nb <= 1024)
 
+// What the one-wave routing (wave_route) uses of a PairBuf: the rank keys of
+// the candidate set A (at most 64) and the entmax candidates' scores (at most
+// as many).  The prefill kernel gives each wave one of these instead of a
+// whole PairBuf, so that more of its workgroups fit in a CU's LDS.
+struct alignas(16) WaveBuf {
+  uint64_t key[64];
+  int rank[64];
+};
+
 struct alignas(16) PairBuf {  // pairwise ranking (16-byte aligned rows)
   union {
     float val[kPairMax + 4];
@@ -1158,9 +1167,9 @@ __device__ __forceinline__ double wave_sum_d(double x) {
 // S = {u > tau} found,
 // accepted only if it satisfies the optimality conditions (u > tau_S on S,
 // u <= tau_S off S), which single out the exact support.
-template <int NS, bool WIDE = false>
+template <int NS, bool WIDE = false, typename Buf = PairBuf>
 __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32_t* o_idx, float* o_prob,
-                                           float* o_bias, int* l_idx, float* l_bias, PairBuf& pb,
+                                           float* o_bias, int* l_idx, float* l_bias, Buf& pb,
                                            unsigned long long* stamps = nullptr) {
   const int lane = threadIdx.x & 63;
   // the routing is the critical path of the step: let this wave win the
@@ -1366,15 +1375,15 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
       tau = readlane_d(tl, __ffsll((unsigned long long)win) - 1);
     } else {
       // u' = (s - smax) / 2 in [-inf, 0]; the root lies in [-1, 0)
-      double up[NS];
-#pragma unroll
-      for (int e = 0; e < NS; ++e) up[e] = ((double)sv[e] - dmax) * 0.5;
+      // u'_e, formed where it is used (the same value every time) rather than
+      // held: 2 NS registers fewer
+      auto up = [&](int e) { return ((double)sv[e] - dmax) * 0.5; };
       double t = -1.0;
       for (int it = 0; it < 64; ++it) {
         double F = 0.0, G = 0.0;
 #pragma unroll
         for (int e = 0; e < NS; ++e) {
-          const double x = fmax(up[e] - t, 0.0);
+          const double x = fmax(up(e) - t, 0.0);
           F = fma(x, x, F);
           G += x;
         }
@@ -1388,21 +1397,21 @@ __device__ __forceinline__ bool wave_route(const float* s, int nb, int kk, int32
       double s1 = 0.0;
 #pragma unroll
       for (int e = 0; e < NS; ++e)
-        if (up[e] > t) {
+        if (up(e) > t) {
           ++r;
-          s1 += up[e];
+          s1 += up(e);
         }
       r = wave_sum(r);
       const double mu = wave_sum_d(s1) / r;
       double ss = 0.0;
 #pragma unroll
       for (int e = 0; e < NS; ++e)
-        if (up[e] > t) ss += (up[e] - mu) * (up[e] - mu);
+        if (up(e) > t) ss += (up(e) - mu) * (up(e) - mu);
       ss = wave_sum_d(ss);
       tau = mu - sqrt(fmax(0.0, (1.0 - ss) / r));
       bool bad = false;
 #pragma unroll
-      for (int e = 0; e < NS; ++e) bad |= (up[e] > t) ? !(up[e] > tau) : (up[e] > tau);
+      for (int e = 0; e < NS; ++e) bad |= (up(e) > t) ? !(up(e) > tau) : (up(e) > tau);
       if (__ballot(bad) != 0) {
         __builtin_amdgcn_s_setprio(0);
         return false;
@@ -1860,15 +1869,23 @@ __global__ __launch_bounds__(kTopkThreads) void k_entmax_topk(TopkArgs a) {
 // come before it.
 // ---------------------------------------------------------------------------
 constexpr int kPrefillThreads = 512;
-constexpr int kPrefillScores = 12288;  // LDS score slots: qt x nb_cap
+// Two builds of the kernel, by the most blocks a query can see (a compile-time
+// bound on the routing's slots per lane, NSMAX): up to 512 blocks with 8 slots
+// per lane the routing fits in 80 registers, so three workgroups (six waves
+// per SIMD) share a CU, with LDS for 16 queries of 512 blocks; up to 1024
+// blocks, 16 slots per lane need 112 registers and the kernel runs two
+// workgroups per CU, with 12288 score slots.
+constexpr int prefill_slots(int nsmax) { return nsmax >= 16 ? 12288 : 16 * 64 * nsmax; }
+constexpr int prefill_nsmax(int nb_cap) { return nb_cap <= 512 ? 8 : 16; }
 constexpr int kPrefillTilesInFlight = 1;  // key tiles per wave with loads in flight (2 or 4 measured slower)
 constexpr int kPrefillMaxQ = 16;
 constexpr int32_t kDeferred = INT32_MIN;
 
+template <int SLOTS>
 struct PrefillSmem {
-  float scores[kPrefillScores];
+  float scores[SLOTS];
   alignas(16) double qidx[kPrefillMaxQ][kIdxDim];
-  PairBuf pb[kPrefillThreads / 64];  // one per wave
+  WaveBuf pb[kPrefillThreads / 64];  // one per wave
   int next_q;                        // next query to route
 };
 
@@ -1929,10 +1946,10 @@ __device__ __forceinline__ void load_key(const float* K, int j, double (&kv)[kId
   }
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArgs a) {
+template <int DT, int D, int NSMAX>
+__global__ __launch_bounds__(kPrefillThreads, NSMAX >= 16 ? 4 : 6) void k_prefill_route(PrefillArgs a) {
   constexpr int W = kPrefillThreads / 64;
-  __shared__ PrefillSmem sm;
+  __shared__ PrefillSmem<prefill_slots(NSMAX)> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const PrefillTile t(a);
   const int nbmax = t.visible(t.nq - 1);
@@ -2053,7 +2070,8 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void k_prefill_route(PrefillArg
       else if (nbq <= 128) ok = wave_route<2, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
       else if (nbq <= 256) ok = wave_route<4, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
       else if (nbq <= 512) ok = wave_route<8, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
-      else if (nbq <= 64 * kWaveBlocks) ok = wave_route<16, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
+      else if constexpr (NSMAX >= 16)
+        if (nbq <= 64 * kWaveBlocks) ok = wave_route<16, true>(sq, nbq, kk, oi, op, ob, nullptr, nullptr, sm.pb[wave]);
       if (!ok && lane == 0) oi[0] = kDeferred;
     }
     int nxt = 0;  // every path through the body claims the next query
@@ -2767,16 +2785,28 @@ hipError_t launch_entmax_topk(const TopkArgs& a, hipStream_t s) {
 }
 
 int prefill_queries_per_wg(int nb_cap) {
-  const int q = nb_cap > 0 ? kPrefillScores / nb_cap : kPrefillMaxQ;
+  const int slots = prefill_nsmax(nb_cap) >= 16 ? prefill_slots(16) : prefill_slots(8);
+  const int q = nb_cap > 0 ? slots / nb_cap : kPrefillMaxQ;
   return q < kPrefillMaxQ ? q : kPrefillMaxQ;
+}
+
+template <int NSMAX>
+hipError_t launch_prefill_tiles(int dtype, int head_dim, const PrefillArgs& a, dim3 grid, hipStream_t s) {
+  if (dtype == 0 && head_dim == 64) k_prefill_route<0, 64, NSMAX><<<grid, kPrefillThreads, 0, s>>>(a);
+  else if (dtype == 0 && head_dim == 128) k_prefill_route<0, 128, NSMAX><<<grid, kPrefillThreads, 0, s>>>(a);
+  else if (dtype == 1 && head_dim == 64) k_prefill_route<1, 64, NSMAX><<<grid, kPrefillThreads, 0, s>>>(a);
+  else if (dtype == 1 && head_dim == 128) k_prefill_route<1, 128, NSMAX><<<grid, kPrefillThreads, 0, s>>>(a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_route(int dtype, int head_dim, const PrefillArgs& a, hipStream_t s) {
   if (a.tq == 0 || a.units == 0) return hipSuccess;
+  if (a.qt != prefill_queries_per_wg(a.nb_cap)) return hipErrorInvalidValue;  // the tile must fit the LDS
   const long long tiles = (a.tq + a.qt - 1) / a.qt;
   const dim3 grid((unsigned)(a.units * tiles));
-  UOCR_DISPATCH(k_prefill_route, grid, dim3(kPrefillThreads), a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = prefill_nsmax(a.nb_cap) >= 16 ? launch_prefill_tiles<16>(dtype, head_dim, a, grid, s)
+                                              : launch_prefill_tiles<8>(dtype, head_dim, a, grid, s);
   if (e != hipSuccess) return e;
   long long passes = ((long long)a.units * a.tq + kPrefillThreads - 1) / kPrefillThreads;
   if (passes > 1024) passes = 1024;
