@@ -106,3 +106,41 @@ def test_prefill_route_wide_entmax_support():
     w = _small(pages=25, planted=10)
     say("prefill route wide support")
     _run(w, 64, [w.prefix_len - 16, w.prefix_len - 40])
+
+
+def test_prefill_route_builds_agree_at_512_blocks():
+    """The kernel is built twice, by the most blocks a query can see: 8 routing
+    slots per lane up to 512 blocks, 16 above.  The same 512-block prefix
+    routed once with a capacity of 512 blocks and once with room for 520 (so
+    the 16-slot build runs) gives the same selections, weights and biases bit
+    for bit; a sample of queries is also checked against the oracle."""
+    need_gpu()
+    w = _small(batch=2, heads=2, pages=64, planted=12)
+    assert w.n_blocks == 512
+    tq = 48
+    q_pos = torch.tensor([w.prefix_len - 32, w.prefix_len - 400], dtype=torch.int32, device="cuda")
+    qs = to_device(S.prefill_queries(w, tq), w.dtype)
+    outs = []
+    for cap in (w.prefix_len, w.prefix_len + 8 * w.block):
+        sess = DecodeSession(w, prefix_cap=cap)
+        say("prefill builds: capacity", cap, "blocks", sess.shape.nb_cap)
+        sess.build_index()
+        outs.append([x.cpu().numpy() for x in sess.prefill_route(qs, q_pos)])
+        del sess
+    torch.cuda.synchronize()
+    for a, b, name in zip(outs[0], outs[1], ("idx", "prob", "bias")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{name} differs between the builds"
+    idx, prob, bias = outs[0][0], outs[0][1].astype(np.float64), outs[0][2].astype(np.float64)
+    P = S.projection(w).astype(np.float64)
+    qd = S.widen(S.prefill_queries(w, tq), w.dtype)
+    pos = q_pos.cpu().numpy()
+    for b in range(w.batch):
+        Kp, _ = S.prefix_kv_seq(w, b)
+        for h in range(w.heads):
+            kb = O.block_index(S.widen(Kp[h], w.dtype), w.prefix_len, P)
+            for i in (0, 1, 2, 3, tq - 1):
+                nbv = O.visible_blocks(int(pos[b]) + i, w.prefix_len)
+                s64 = O.block_scores(qd[b, h, i], P, kb[:nbv])
+                eps = O.score_error_bound(qd[b, h, i], P, kb[:nbv])
+                _check_selection(idx[b, h, i], prob[b, h, i], bias[b, h, i], O.as_f32(s64), w.topk, s64, eps,
+                                 f"builds b={b} h={h} i={i}")
